@@ -1,0 +1,177 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) small-M NVFP4 W4A4 decode linear.
+ *
+ * The operation: "ReSET: Accurate Latency-Critical NVFP4 Reasoning via
+ * Step-Aware Temperature Scaling", GitHub README, section "Core components",
+ * item 2 (kernels/, nvfp4r): a decode linear y = x W^T for M <= 8 activation
+ * rows in which both operands are NVFP4 (W4A4), computed by streaming the FP4
+ * weights once and reusing every loaded weight for all M rows.  The arXiv
+ * abstract states the same problem (small-M NVFP4 kernel for latency-critical
+ * autoregressive decoding).  The same README's "Quantize a model to NVFP4"
+ * section covers converting bf16 weights to NVFP4 offline.
+ *
+ * Number format (the pages name NVFP4 without defining it; the public NVFP4
+ * layout is used): element = E2M1 code (OCP MX v1.0, 5.3.3), one E4M3 ("FN",
+ * OCP OFP8) scale per 16 consecutive elements along K, one binary32 scale per
+ * tensor.  x_hat = e2m1(code) * e4m3(scale) * gscale.
+ *
+ * Quantizer Q(X) for a bf16 tensor X [R][K] (every step binary32, round to
+ * nearest even, no fused multiply-add, denormals kept):
+ *   A = max|x| over the tensor;  gscale = A / 2688 (= 6 * 448), 1 if that is 0
+ *   per 16-block: a = max|x|; sigma = a / (gscale * 6);
+ *     scale byte = E4M3 round-to-nearest-even of sigma, saturating at 448;
+ *     T = e4m3(scale) * gscale;  r = (T == 0) ? 0 : 1 / T;
+ *     code = E2M1 round-to-nearest-even of x * r, saturating at 6, sign bit
+ *     taken from x (so -0 gives code 0x8).
+ *
+ * Canonical layouts (row-major, used for activations and for export):
+ *   codes  [R][K/2]  byte i holds element 2i in bits 0..3, 2i+1 in bits 4..7
+ *   scales [R][K/16] one E4M3 byte per block
+ *
+ * Device-tiled weight layout (layout version 1), padded to N_pad = 32 *
+ * ceil(N/32) rows and K_pad = 256 * ceil(K/256) columns; padding holds code 0
+ * and scale 0:
+ *   codes:  1024-byte records, record (t, c) at byte (t * K_pad/64 + c) * 1024
+ *           for row tile t (rows 32t..32t+31) and K chunk c (64 elements).
+ *           Inside a record, the 16 bytes at 16 * l (l = 0..63) hold row
+ *           32t + (l % 32), elements 64c + 32*(l / 32) + 0..31, packed as in
+ *           the canonical layout.
+ *   scales: 512-byte records, record (t, g) at byte (t * K_pad/256 + g) * 512
+ *           for K group g (256 elements).  The 8 bytes at 8 * l hold the
+ *           scales of row 32t + (l % 32), blocks 16g + 4q + 2*(l / 32) + b
+ *           at byte 2q + b (q = 0..3, b = 0..1).
+ *   So every 64-lane wavefront load of a record is one contiguous 1 KiB
+ *   (codes) or 512 B (scales), and lane l's code bytes in chunk c are covered
+ *   by its own scale bytes.
+ *
+ * Conventions:
+ *   - Pointers are device pointers unless a comment says "host".  The caller
+ *     owns every buffer; no entry point allocates device memory or
+ *     synchronizes the device, except the stack object (nvfp4_stack_*), which
+ *     allocates its activation buffers once at creation.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; every call in the linear and
+ *     quantization paths can be captured into a HIP graph.
+ *   - Argument errors are detected on the host before any HIP call and
+ *     return without enqueuing work.  A failing HIP call returns
+ *     NVFP4_ERR_HIP; its hipError_t is kept per host thread
+ *     (nvfp4_last_hip_error).  Device faults surface at the caller's next
+ *     synchronization, as for any HIP kernel.
+ *   - Inputs must be finite.  A tensor amax in (0, 2^-90) is outside the
+ *     contract (1/T may overflow): codes are then unspecified, never a crash.
+ */
+#ifndef NVFP4_DECODE_LINEAR_H
+#define NVFP4_DECODE_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment      */
+  NVFP4_ERR_UNSUPPORTED = 2, /* M > 8, device is not gfx950, unknown option */
+  NVFP4_ERR_NO_DEVICE = 3,   /* no HIP device visible                      */
+  NVFP4_ERR_WORKSPACE = 4,   /* workspace smaller than required            */
+  NVFP4_ERR_HIP = 5          /* a HIP runtime call failed                  */
+} nvfp4_status;
+
+typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
+
+/* Runtime knobs (process-global, atomic).  Counterpart of the README's
+ * "nvfp4r.configure(gemv_max_m=2)" / "nvfp4r.status()" (section "Run
+ * benchmarks", the Python wiring example). */
+typedef enum {
+  NVFP4_OPT_GEMV_MAX_M = 0,   /* M <= value uses the VALU GEMV; larger M uses
+                                 the MFMA skinny GEMM.  Default 8; 0..8.   */
+  NVFP4_OPT_SPLIT_K = 1,      /* 0 = heuristic; s >= 1 forces s K-slices.  */
+  NVFP4_OPT_CHUNKS_PER_WAVE = 2, /* 0 = heuristic; else 64-element K chunks
+                                 each wavefront streams per row tile (multiple
+                                 of 4).                                     */
+  NVFP4_OPT_NONTEMPORAL = 3,  /* 1 (default) = stream weights with
+                                 non-temporal loads; 0 = ordinary loads.   */
+  NVFP4_OPT_COUNT = 4
+} nvfp4_option;
+
+/* ABI version of this header (incremented on any signature change). */
+int nvfp4_abi_version(void);
+
+/* Version of the device-tiled weight layout described above (1). */
+int nvfp4_layout_version(void);
+
+/* Static, never-freed description of a status code. */
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* hipError_t of the last failing HIP call on this host thread (0 if none). */
+int nvfp4_last_hip_error(void);
+
+/* Set / read a runtime knob.  Unknown option or out-of-range value:
+ * NVFP4_ERR_UNSUPPORTED / NVFP4_ERR_INVALID_ARG.  `value` is a host pointer. */
+nvfp4_status nvfp4_set_option(int opt, int64_t value);
+nvfp4_status nvfp4_get_option(int opt, int64_t* value);
+
+/* Bytes of the device-tiled codes and scales for an N x K weight (host
+ * outputs).  N >= 1, K >= 16, K % 16 == 0. */
+nvfp4_status nvfp4_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_t* scales_bytes);
+
+/* Weight quantization, once per model load (README "Quantize a model to
+ * NVFP4": bf16 checkpoint -> NVFP4).
+ *   w_bf16   [N][ldw] bf16 bit patterns, ldw >= K, row r at w_bf16 + r*ldw
+ *   w_codes  device-tiled codes  (nvfp4_weight_bytes bytes)
+ *   w_scales device-tiled scales (nvfp4_weight_bytes bytes)
+ *   w_gscale one float, written on the device
+ * Enqueues four kernels (init, tensor amax, blocks, finalize). */
+nvfp4_status nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* w_codes, uint8_t* w_scales, float* w_gscale,
+                                   void* stream);
+
+/* Inverse of the tiling: device-tiled weight -> canonical row-major codes
+ * [N][K/2] and scales [N][K/16] (for export and bit-exact checks). */
+nvfp4_status nvfp4_unpack_weight(const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                 int64_t K, uint8_t* codes_rowmajor, uint8_t* scales_rowmajor,
+                                 void* stream);
+
+/* Activation quantization, every decode step (W4A4: the activations reach
+ * the linear as NVFP4).  One tensor scale over the whole M x K input.
+ *   x_bf16   [M][ldx] bf16, 1 <= M <= 8, ldx >= K, ldx % 8 == 0, 16-byte
+ *            aligned base
+ *   x_codes  [M][K/2] canonical;  x_scales [M][K/16] canonical
+ *   x_gscale one float, written on the device (never read back to the host)
+ */
+nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                void* stream);
+
+/* Workspace bytes nvfp4_linear needs for this shape under the current
+ * options (split-K partial sums and arrival counters).  0 is possible. */
+size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K);
+
+/* Zero a workspace before its first use (a fill kernel on `stream`).  The
+ * split-K counters reset themselves afterwards, so one initialisation covers
+ * any number of later calls, graph replays included.  One workspace must not
+ * be used by two calls that can run concurrently. */
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* The decode linear y[m][n] = xgs * wgs * sum_k x[m][k] w[n][k] over the
+ * dequantized NVFP4 operands, 1 <= M <= 8.
+ *   x_codes/x_scales canonical activation ([M][K/2], [M][K/16]); x_gscale
+ *   and w_gscale device floats; w_codes/w_scales device-tiled weight;
+ *   y [M][N] row-major, binary32 or bf16 (round to nearest even);
+ *   workspace as sized by nvfp4_linear_workspace_bytes and initialised once
+ *   by nvfp4_workspace_init.
+ * Accuracy: |y - y_exact| <= 1e-3 * sum_k |x_hat w_hat| per element (plus
+ * half a bf16 ulp for bf16 output); the result is bit-identical from run to
+ * run (fixed-order split-K reduction). */
+nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
+                          const uint8_t* x_scales, const float* x_gscale, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* w_gscale, void* y, int out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_DECODE_LINEAR_H */

@@ -1,0 +1,225 @@
+"""Python binding of libnvfp4.so, the MI355X (gfx950) small-M NVFP4 W4A4
+decode linear ("ReSET" GitHub README, "Core components", item 2).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/nvfp4.h.  torch supplies device memory
+and the current HIP stream.  There is no fallback: if the library is not
+built, importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_WORKSPACE, ERR_HIP = range(6)
+OUT_F32, OUT_BF16 = 0, 1
+OPTIONS = {"gemv_max_m": 0, "split_k": 1, "chunks_per_wave": 2, "nontemporal": 3}
+TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(python -m nvfp4_decode_linear_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_c_i64, _c_int, _c_size, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_abi_version = _sig("nvfp4_abi_version", _c_int)
+_layout_version = _sig("nvfp4_layout_version", _c_int)
+_status_string = _sig("nvfp4_status_string", ctypes.c_char_p, _c_int)
+_last_hip_error = _sig("nvfp4_last_hip_error", _c_int)
+_set_option = _sig("nvfp4_set_option", _c_int, _c_int, _c_i64)
+_get_option = _sig("nvfp4_get_option", _c_int, _c_int, ctypes.POINTER(_c_i64))
+_weight_bytes = _sig("nvfp4_weight_bytes", _c_int, _c_i64, _c_i64, ctypes.POINTER(_c_size),
+                     ctypes.POINTER(_c_size))
+_quantize_weight = _sig("nvfp4_quantize_weight", _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp,
+                        _vp, _vp)
+_unpack_weight = _sig("nvfp4_unpack_weight", _c_int, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp)
+_quantize_act = _sig("nvfp4_quantize_act", _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
+                     _vp)
+_linear_workspace_bytes = _sig("nvfp4_linear_workspace_bytes", _c_size, _c_int, _c_i64, _c_i64)
+_workspace_init = _sig("nvfp4_workspace_init", _c_int, _vp, _c_size, _vp)
+_linear = _sig("nvfp4_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+               _c_int, _vp, _c_size, _vp)
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise NVFP4Error(status, where)
+
+
+def abi_version() -> int:
+    return _abi_version()
+
+
+def layout_version() -> int:
+    return _layout_version()
+
+
+def set_option(name, value: int) -> None:
+    _check(_set_option(OPTIONS.get(name, name), int(value)), "nvfp4_set_option")
+
+
+def get_option(name) -> int:
+    v = _c_i64()
+    _check(_get_option(OPTIONS.get(name, name), ctypes.byref(v)), "nvfp4_get_option")
+    return v.value
+
+
+def weight_bytes(N: int, K: int):
+    c, s = _c_size(), _c_size()
+    _check(_weight_bytes(N, K, ctypes.byref(c), ctypes.byref(s)), "nvfp4_weight_bytes")
+    return c.value, s.value
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return _linear_workspace_bytes(M, N, K)
+
+
+# ------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class QuantWeight:
+    """Device-tiled NVFP4 weight (layout version 1)."""
+    codes: object      # uint8 tensor, tiled
+    scales: object     # uint8 tensor, tiled
+    gscale: object     # float32 tensor [1]
+    N: int
+    K: int
+
+
+@dataclass
+class QuantAct:
+    """Canonical NVFP4 activation: codes [M][K/2], scales [M][K/16]."""
+    codes: object
+    scales: object
+    gscale: object     # float32 tensor [1]
+    M: int
+    K: int
+
+
+def empty_weight(N: int, K: int, device="cuda") -> QuantWeight:
+    torch = _torch()
+    cb, sb = weight_bytes(N, K)
+    return QuantWeight(torch.empty(cb, dtype=torch.uint8, device=device),
+                       torch.empty(sb, dtype=torch.uint8, device=device),
+                       torch.empty(1, dtype=torch.float32, device=device), N, K)
+
+
+def quantize_weight(w, out: QuantWeight | None = None) -> QuantWeight:
+    """bf16 [N][K] (row stride >= K) -> device-tiled NVFP4 weight."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D bf16 tensor with unit column stride")
+    N, K = w.shape
+    q = out if out is not None else empty_weight(N, K, w.device)
+    _check(_quantize_weight(_ptr(w), N, K, w.stride(0), _ptr(q.codes), _ptr(q.scales),
+                            _ptr(q.gscale), _stream(w)), "nvfp4_quantize_weight")
+    return q
+
+
+def unpack_weight(q: QuantWeight):
+    """Device-tiled weight -> canonical (codes [N][K/2], scales [N][K/16])."""
+    torch = _torch()
+    c = torch.empty((q.N, q.K // 2), dtype=torch.uint8, device=q.codes.device)
+    s = torch.empty((q.N, q.K // 16), dtype=torch.uint8, device=q.codes.device)
+    _check(_unpack_weight(_ptr(q.codes), _ptr(q.scales), q.N, q.K, _ptr(c), _ptr(s),
+                          _stream(c)), "nvfp4_unpack_weight")
+    return c, s
+
+
+def empty_act(M: int, K: int, device="cuda") -> QuantAct:
+    torch = _torch()
+    return QuantAct(torch.empty((M, K // 2), dtype=torch.uint8, device=device),
+                    torch.empty((M, K // 16), dtype=torch.uint8, device=device),
+                    torch.empty(1, dtype=torch.float32, device=device), M, K)
+
+
+def quantize_act(x, out: QuantAct | None = None) -> QuantAct:
+    """bf16 [M][K] (row stride >= K, multiple of 8) -> canonical NVFP4 with
+    one tensor scale computed on the device."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    q = out if out is not None else empty_act(M, K, x.device)
+    _check(_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q.codes), _ptr(q.scales),
+                         _ptr(q.gscale), _stream(x)), "nvfp4_quantize_act")
+    return q
+
+
+_WS = {}
+
+
+def workspace(M: int, N: int, K: int, device="cuda"):
+    """A per-device workspace, grown and zero-initialised on demand."""
+    torch = _torch()
+    need = linear_workspace_bytes(M, N, K)
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace_init(ws)
+        _WS[key] = ws
+    return ws
+
+
+def workspace_init(ws) -> None:
+    _check(_workspace_init(_ptr(ws), ws.numel(), _stream(ws)), "nvfp4_workspace_init")
+
+
+def linear(xq: QuantAct, wq: QuantWeight, out_dtype=None, out=None, ws=None):
+    """y [M][N] = NVFP4 linear of the quantized activation and weight."""
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    if xq.K != wq.K:
+        raise ValueError("K mismatch")
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    y = out if out is not None else torch.empty((xq.M, wq.N), dtype=out_dtype,
+                                                device=wq.codes.device)
+    if ws is None:
+        ws = workspace(xq.M, wq.N, wq.K, wq.codes.device)
+    _check(_linear(xq.M, wq.N, wq.K, _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.gscale),
+                   _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), od, _ptr(ws),
+                   ws.numel(), _stream(y)), "nvfp4_linear")
+    return y

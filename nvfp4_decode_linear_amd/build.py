@@ -1,0 +1,67 @@
+"""Build libnvfp4.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Compiles every source under csrc/ in-tree (object files under _build/) and
+links the shared library next to this file.  Run as
+``python -m nvfp4_decode_linear_amd.build`` or through
+``__graft_entry__.build()``.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libnvfp4.so")
+ARCH = "gfx950"
+
+# -ffp-contract=off: the quantizer's binary32 steps must not fuse into fma.
+# Packed fp32 instructions are disabled for every HIP translation unit.
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", "-Wno-unused-function"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libnvfp4.so)")
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def _compile(hipcc: str, src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
+    if src.endswith(".hip"):
+        cmd[1:1] = DEVICE
+    subprocess.run(cmd, check=True)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    """Compile and link; returns the library path.  Always rebuilds."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(hipcc, s), srcs))
+    tmp = LIB + ".tmp"
+    subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                   check=True)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,234 @@
+// C ABI of the NVFP4 decode-linear library (include/nvfp4.h): argument
+// validation on the host before any HIP call, runtime knobs, launch plans,
+// and dispatch to the gfx950 kernels.  The runtime knobs follow the README's
+// "nvfp4r.configure(gemv_max_m=2)" / "nvfp4r.status()" example ("ReSET"
+// GitHub README, "Run benchmarks").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/nvfp4.h"
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+using nvfp4::GemvPlan;
+using nvfp4::round_up;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kLayoutVersion = 1;
+constexpr int kMaxM = 8;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{8}, {0}, {0}, {1}};
+thread_local int t_last_hip = 0;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+nvfp4_status hip_fail(hipError_t e) {
+  t_last_hip = (int)e;
+  return NVFP4_ERR_HIP;
+}
+
+// Current device must be a gfx950; cached per device.
+nvfp4_status check_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n == 0) return NVFP4_ERR_NO_DEVICE;
+    return hip_fail(e);
+  }
+  if (dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    const hipError_t pe = hipGetDeviceProperties(&prop, dev);
+    if (pe != hipSuccess) return hip_fail(pe);
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_nk(int64_t N, int64_t K) {
+  return N >= 1 && K >= 16 && K % 16 == 0 && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30) &&
+         round_up(N, nvfp4::kTileN) * round_up(K, nvfp4::kGroupK) / 2 <= (int64_t(1) << 40);
+}
+
+// Launch plan of the VALU GEMV for (M, N, K) under the current knobs.
+GemvPlan make_plan(int M, int64_t N, int64_t K) {
+  GemvPlan p;
+  p.kc = (int)(round_up(K, nvfp4::kGroupK) / nvfp4::kChunkK);
+  p.tiles = (int)(round_up(N, nvfp4::kTileN) / nvfp4::kTileN);
+  p.waves = 4;
+  p.nontemporal = g_opts[NVFP4_OPT_NONTEMPORAL].load() ? 1 : 0;
+  const int64_t force_cpw = g_opts[NVFP4_OPT_CHUNKS_PER_WAVE].load();
+  const int64_t force_split = g_opts[NVFP4_OPT_SPLIT_K].load();
+  // Enough workgroups to give every one of the 256 CUs two, with each
+  // wavefront streaming as many 1 KiB records as possible (<= 16).
+  const int64_t want_wgs = 512;
+  int cpw = 4;
+  if (force_cpw > 0) {
+    cpw = (int)force_cpw;
+  } else if (force_split > 0) {
+    const int64_t per = (p.kc + force_split - 1) / force_split;          // chunks per slice
+    cpw = (int)std::min<int64_t>(16, std::max<int64_t>(4, round_up((per + 3) / 4, 4)));
+  } else {
+    const int cands[4] = {16, 12, 8, 4};
+    for (int c : cands) {
+      const int64_t splits = (p.kc + 4 * c - 1) / (4 * c);
+      if ((int64_t)p.tiles * splits >= want_wgs) { cpw = c; break; }
+    }
+  }
+  // LDS per workgroup: the decoded activation slice (M * cps * 64 f16) plus
+  // the cross-wave reduction buffer; kept within 64 KiB.
+  while (cpw > 4 && (int64_t)M * cpw * p.waves * 128 + (int64_t)p.waves * M * 128 + 64 > 65536)
+    cpw -= 4;
+  p.cpw = cpw;
+  p.cps = cpw * p.waves;
+  p.splits = (p.kc + p.cps - 1) / p.cps;
+  const int64_t n_pad = (int64_t)p.tiles * nvfp4::kTileN;
+  p.ws_partials = p.splits > 1 ? (size_t)round_up((int64_t)p.splits * M * n_pad * 4, 256) : 0;
+  p.ws_bytes = p.splits > 1 ? p.ws_partials + (size_t)round_up((int64_t)p.tiles * 4, 256) : 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return kAbiVersion; }
+int nvfp4_layout_version(void) { return kLayoutVersion; }
+int nvfp4_last_hip_error(void) { return t_last_hip; }
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported (M > 8, not a gfx950 device, or unknown option)";
+    case NVFP4_ERR_NO_DEVICE: return "no HIP device";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_HIP: return "HIP runtime error (see nvfp4_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+nvfp4_status nvfp4_set_option(int opt, int64_t value) {
+  switch (opt) {
+    case NVFP4_OPT_GEMV_MAX_M:
+      if (value < 0 || value > kMaxM) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_SPLIT_K:
+      if (value < 0 || value > 4096) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_CHUNKS_PER_WAVE:
+      if (value < 0 || value > 16 || value % 4) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_NONTEMPORAL:
+      if (value != 0 && value != 1) return NVFP4_ERR_INVALID_ARG;
+      break;
+    default: return NVFP4_ERR_UNSUPPORTED;
+  }
+  g_opts[opt].store(value);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_get_option(int opt, int64_t* value) {
+  if (opt < 0 || opt >= NVFP4_OPT_COUNT) return NVFP4_ERR_UNSUPPORTED;
+  if (!value) return NVFP4_ERR_INVALID_ARG;
+  *value = g_opts[opt].load();
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_t* scales_bytes) {
+  if (!codes_bytes || !scales_bytes || !valid_nk(N, K)) return NVFP4_ERR_INVALID_ARG;
+  const int64_t np = round_up(N, nvfp4::kTileN), kp = round_up(K, nvfp4::kGroupK);
+  *codes_bytes = (size_t)(np * kp / 2);
+  *scales_bytes = (size_t)(np * kp / 16);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* w_codes, uint8_t* w_scales, float* w_gscale,
+                                   void* stream) {
+  if (!w_bf16 || !w_codes || !w_scales || !w_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (!valid_nk(N, K) || ldw < K || ldw % 8 != 0) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(w_bf16, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
+      !aligned(w_gscale, 4))
+    return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_quantize_weight(w_bf16, N, K, ldw, w_codes, w_scales,
+                                                     w_gscale, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_unpack_weight(const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                 int64_t K, uint8_t* codes_rowmajor, uint8_t* scales_rowmajor,
+                                 void* stream) {
+  if (!w_codes || !w_scales || !codes_rowmajor || !scales_rowmajor) return NVFP4_ERR_INVALID_ARG;
+  if (!valid_nk(N, K)) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 8) || !aligned(codes_rowmajor, 8)) return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_unpack_weight(w_codes, w_scales, N, K, codes_rowmajor,
+                                                   scales_rowmajor, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                void* stream) {
+  if (!x_bf16 || !x_codes || !x_scales || !x_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || K < 16 || K % 16 != 0 || K > (int64_t(1) << 28) || ldx < K || ldx % 8 != 0)
+    return M > kMaxM ? NVFP4_ERR_UNSUPPORTED : NVFP4_ERR_INVALID_ARG;
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4))
+    return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_quantize_act(x_bf16, M, (int)K, ldx, x_codes, x_scales,
+                                                  x_gscale, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxM || !valid_nk(N, K)) return 0;
+  return make_plan(M, N, K).ws_bytes;
+}
+
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return NVFP4_OK;
+  if (!workspace || !aligned(workspace, 4)) return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_fill_zero(workspace, workspace_bytes, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
+                          const uint8_t* x_scales, const float* x_gscale, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* w_gscale, void* y, int out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (M < 1 || !valid_nk(N, K) || N > (int64_t(1) << 28) || K > (int64_t(1) << 28))
+    return NVFP4_ERR_INVALID_ARG;
+  if (!x_codes || !x_scales || !x_gscale || !w_codes || !w_scales || !w_gscale || !y)
+    return NVFP4_ERR_INVALID_ARG;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_codes, 8) || !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
+      !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
+    return NVFP4_ERR_INVALID_ARG;
+  const GemvPlan p = make_plan(M, N, K);
+  if (p.ws_bytes > 0) {
+    if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < p.ws_bytes) return NVFP4_ERR_WORKSPACE;
+  }
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_gemv_valu(p, M, N, K, x_codes, x_scales, x_gscale, w_codes,
+                                               w_scales, w_gscale, y, out_dtype, workspace,
+                                               (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+}  // extern "C"

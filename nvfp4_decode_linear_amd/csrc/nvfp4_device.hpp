@@ -1,0 +1,155 @@
+// Device-side helpers shared by the NVFP4 kernels (gfx950 only).
+//
+// Format: NVFP4 as used by the small-M W4A4 decode linear of "ReSET:
+// Accurate Latency-Critical NVFP4 Reasoning via Step-Aware Temperature
+// Scaling" (GitHub README, "Core components", item 2): E2M1 elements (OCP MX
+// v1.0, 5.3.3), one E4M3 "FN" scale (OCP OFP8 v1.0) per 16 elements along K,
+// one binary32 scale per tensor.  The quantizer arithmetic below must stay
+// bit-identical to the IEEE reading documented in include/nvfp4.h: every
+// step is one correctly rounded binary32 operation (explicit __fdiv_rn /
+// __fmul_rn, the translation unit is built with -ffp-contract=off and keeps
+// binary32 denormals).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Tiled weight layout (layout version 1; see include/nvfp4.h).
+constexpr int kTileN = 32;          // rows per tile
+constexpr int kChunkK = 64;         // elements per 1 KiB code record row-pair
+constexpr int kGroupK = 256;        // elements per 512 B scale record
+constexpr int kCodeRecord = 1024;   // bytes
+constexpr int kScaleRecord = 512;   // bytes
+constexpr int kWave = 64;
+
+// 6 * 448: largest E2M1 magnitude times largest E4M3 scale.
+constexpr float kAmaxToScale = 2688.0f;
+
+// ---------------------------------------------------------------- codecs
+
+// E4M3 byte (0x00..0x7E) -> binary32, exact.
+__host__ __device__ inline float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = b >> 3, m = b & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9, exact
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Non-negative finite binary32 -> E4M3 byte: nearest, ties to even mantissa,
+// saturating at 448 (0x7E).
+__device__ inline uint32_t f32_to_e4m3_rne_sat(float sigma) {
+  sigma = fminf(sigma, 448.0f);
+  if (sigma < 0.015625f) {                       // below 2^-6: grid m * 2^-9
+    // sigma * 512 is exact; rint rounds half to even.  8 -> 0x08 (2^-6).
+    return (uint32_t)__builtin_rintf(__fmul_rn(sigma, 512.0f));
+  }
+  uint32_t u = __float_as_uint(sigma);
+  u += 0x7FFFFu + ((u >> 20) & 1u);              // keep 3 mantissa bits, RNE
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// binary32 -> E2M1 code: nearest magnitude of {0,.5,1,1.5,2,3,4,6}, ties to
+// the even code, saturating at 6; sign bit from the sign of y.
+__device__ inline uint32_t f32_to_e2m1_rne_sat(float y) {
+  const float a = fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Tensor scale from the tensor amax: amax / 2688, replaced by 1 when 0.
+__device__ inline float tensor_scale(float amax) {
+  float sg = __fdiv_rn(amax, kAmaxToScale);
+  return sg == 0.0f ? 1.0f : sg;
+}
+
+struct BlockQ {
+  uint32_t scale;     // E4M3 byte
+  uint32_t lo, hi;    // 16 packed E2M1 codes (element 2i in the low nibble)
+};
+
+// Quantize one 16-element block of bf16 values (8 packed pairs) given the
+// tensor scale: sigma = a / (sg*6); scale = E4M3(sigma); T = S*sg;
+// r = 1/T (0 if T == 0); code_i = E2M1(x_i * r).
+__device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], float sg) {
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = v[i] & 0x7FFF7FFFu;          // |x| as ordered integers
+    amax_bits = max(amax_bits, max(a & 0xFFFFu, a >> 16));
+  }
+  const float a = __uint_as_float(amax_bits << 16);
+  const float d = __fmul_rn(sg, 6.0f);
+  const uint32_t sb = f32_to_e4m3_rne_sat(__fdiv_rn(a, d));
+  const float T = __fmul_rn(e4m3_to_f32(sb), sg);
+  const float r = (T == 0.0f) ? 0.0f : __fdiv_rn(1.0f, T);
+  BlockQ q;
+  q.scale = sb;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x0 = __uint_as_float(v[i] << 16);
+    const float x1 = __uint_as_float(v[i] & 0xFFFF0000u);
+    const uint32_t c0 = f32_to_e2m1_rne_sat(__fmul_rn(x0, r));
+    const uint32_t c1 = f32_to_e2m1_rne_sat(__fmul_rn(x1, r));
+    w[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+  }
+  q.lo = w[0];
+  q.hi = w[1];
+  return q;
+}
+
+// Same for a block given as 16 binary32 values (fused stack kernels).
+__device__ inline BlockQ quantize_block_f32(const float (&x)[16], float sg) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float d = __fmul_rn(sg, 6.0f);
+  const uint32_t sb = f32_to_e4m3_rne_sat(__fdiv_rn(a, d));
+  const float T = __fmul_rn(e4m3_to_f32(sb), sg);
+  const float r = (T == 0.0f) ? 0.0f : __fdiv_rn(1.0f, T);
+  BlockQ q;
+  q.scale = sb;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = f32_to_e2m1_rne_sat(__fmul_rn(x[i], r));
+    w[i >> 3] |= c << (4 * (i & 7));
+  }
+  q.lo = w[0];
+  q.hi = w[1];
+  return q;
+}
+
+// ---------------------------------------------------------- reductions
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// binary32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+}  // namespace nvfp4

@@ -1,0 +1,224 @@
+// NVFP4 quantization kernels for gfx950: activation quantizer (every decode
+// step), weight quantizer into the device-tiled layout (once per model
+// load), the inverse tiling, and a zero-fill.
+//
+// The quantizer reading (tensor amax -> tensor scale; per 16-block E4M3
+// scale; per element E2M1 code, all binary32, round to nearest even) is the
+// one documented in include/nvfp4.h.  W4A4 = both operands of the decode
+// linear are NVFP4: "ReSET" GitHub README, "Core components", item 2; the
+// weights are converted offline: README, "Quantize a model to NVFP4".
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline void load_block_bf16(const uint16_t* p, uint32_t (&v)[8]) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 8);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ inline uint32_t absmax_bits(const uint32_t (&v)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = v[i] & 0x7FFF7FFFu;
+    m = max(m, max(a & 0xFFFFu, a >> 16));
+  }
+  return m;
+}
+
+// ------------------------------------------------------------ activations
+//
+// One workgroup quantizes the whole M x K activation: pass 1 takes the
+// tensor amax (bf16 magnitudes compared as integers, exact), pass 2
+// re-reads each 16-block (an L2 hit) and writes its scale and codes.  The
+// tensor scale never leaves the device.
+constexpr int kActThreads = 1024;
+
+__global__ __launch_bounds__(kActThreads) void act_quant_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale) {
+  __shared__ uint32_t red[kActThreads / kWave];
+  const int nbr = K >> 4;
+  const int nb = M * nbr;
+  uint32_t amax = 0;
+  for (int b = threadIdx.x; b < nb; b += kActThreads) {
+    const int m = b / nbr, j = b - m * nbr;
+    uint32_t v[8];
+    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
+    amax = max(amax, absmax_bits(v));
+  }
+  amax = wave_max_u32(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  uint32_t all = 0;
+#pragma unroll
+  for (int w = 0; w < kActThreads / kWave; ++w) all = max(all, red[w]);
+  const float sg = tensor_scale(bf16_to_f32(all));
+  if (threadIdx.x == 0) *gscale = sg;
+  for (int b = threadIdx.x; b < nb; b += kActThreads) {
+    const int m = b / nbr, j = b - m * nbr;
+    uint32_t v[8];
+    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
+    const BlockQ q = quantize_block_bf16(v, sg);
+    u32x2 c;
+    c.x = q.lo;
+    c.y = q.hi;
+    *reinterpret_cast<u32x2*>(codes + (int64_t)m * (K >> 1) + 8 * j) = c;
+    scales[(int64_t)m * nbr + j] = (uint8_t)q.scale;
+  }
+}
+
+// ---------------------------------------------------------------- weights
+
+__global__ void wq_init_kernel(uint32_t* slot) { *slot = 0u; }
+
+// Tensor amax of the bf16 weight; the slot holds the binary32 bits of the
+// running maximum (non-negative floats order like their bit patterns).
+__global__ __launch_bounds__(256) void wq_amax_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                      int64_t K, int64_t ldw, uint32_t* slot) {
+  const int64_t vpr = K >> 3;
+  const int64_t total = N * vpr;
+  uint32_t amax = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / vpr, v = i - r * vpr;
+    const u32x4 q = *reinterpret_cast<const u32x4*>(w + r * ldw + 8 * v);
+    const uint32_t t[4] = {q.x & 0x7FFF7FFFu, q.y & 0x7FFF7FFFu, q.z & 0x7FFF7FFFu,
+                           q.w & 0x7FFF7FFFu};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) amax = max(amax, max(t[k] & 0xFFFFu, t[k] >> 16));
+  }
+  amax = wave_max_u32(amax);
+  if ((threadIdx.x & 63) == 0 && amax != 0u) atomicMax(slot, amax << 16);
+}
+
+// One thread per (row tile, K chunk, lane): quantizes the two 16-blocks the
+// lane owns in the tiled layout and writes its 16 code bytes and 2 scale
+// bytes.  Padding rows and columns are written as zeros.
+__global__ __launch_bounds__(256) void wq_blocks_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                        int64_t K, int64_t ldw, int kc, int kg,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales,
+                                                        const uint32_t* __restrict__ slot) {
+  const float sg = tensor_scale(__uint_as_float(*slot));
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rec = gid >> 6;
+  const int l = (int)(gid & 63);
+  const int64_t t = rec / kc;
+  const int c = (int)(rec - t * kc);
+  const int64_t n = t * kTileN + (l & 31);
+  const int64_t k0 = (int64_t)c * kChunkK + 32 * (l >> 5);
+  u32x4 out = {0u, 0u, 0u, 0u};
+  uint32_t sc = 0;
+  if (n < N) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t kb = k0 + 16 * b;
+      if (kb < K) {
+        uint32_t v[8];
+        load_block_bf16(w + n * ldw + kb, v);
+        const BlockQ q = quantize_block_bf16(v, sg);
+        out[2 * b] = q.lo;
+        out[2 * b + 1] = q.hi;
+        sc |= q.scale << (8 * b);
+      }
+    }
+  }
+  *reinterpret_cast<u32x4*>(codes + rec * kCodeRecord + 16 * l) = out;
+  const int g = c >> 2, q = c & 3;
+  *reinterpret_cast<uint16_t*>(scales + (t * kg + g) * kScaleRecord + 8 * l + 2 * q) =
+      (uint16_t)sc;
+}
+
+__global__ void wq_finalize_kernel(uint32_t* slot) {
+  const float sg = tensor_scale(__uint_as_float(*slot));
+  *reinterpret_cast<float*>(slot) = sg;
+}
+
+// Tiled -> canonical, one thread per (row, 16-block).
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t N,
+                                                     int64_t K, int kc, int kg,
+                                                     uint8_t* __restrict__ codes_rm,
+                                                     uint8_t* __restrict__ scales_rm) {
+  const int64_t nbr = K >> 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= N * nbr) return;
+  const int64_t n = gid / nbr, j = gid - n * nbr;
+  const int64_t t = n / kTileN;
+  const int r = (int)(n - t * kTileN);
+  const int64_t k = 16 * j;
+  const int64_t c = k / kChunkK;
+  const int h = (int)((k % kChunkK) / 32), b = (int)((k % 32) / 16);
+  const int l = r + 32 * h;
+  const u32x2 v =
+      *reinterpret_cast<const u32x2*>(codes + (t * kc + c) * kCodeRecord + 16 * l + 8 * b);
+  *reinterpret_cast<u32x2*>(codes_rm + n * (K >> 1) + 8 * j) = v;
+  const int64_t g = k / kGroupK;
+  const int q = (int)((k % kGroupK) / kChunkK);
+  scales_rm[n * nbr + j] = scales[(t * kg + g) * kScaleRecord + 8 * l + 2 * q + b];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
+                               uint8_t* scales, float* gscale, hipStream_t s) {
+  hipLaunchKernelGGL(act_quant_kernel, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx, codes,
+                     scales, gscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s) {
+  uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
+  const int64_t n_pad = round_up(N, kTileN), k_pad = round_up(K, kGroupK);
+  const int kc = (int)(k_pad / kChunkK), kg = (int)(k_pad / kGroupK);
+  hipLaunchKernelGGL(wq_init_kernel, dim3(1), dim3(1), 0, s, slot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t vecs = N * (K >> 3);
+  const int64_t amax_blocks = std::min<int64_t>((vecs + 255) / 256, 4096);
+  hipLaunchKernelGGL(wq_amax_kernel, dim3((unsigned)amax_blocks), dim3(256), 0, s, w, N, K, ldw,
+                     slot);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t threads = (n_pad / kTileN) * kc * kWave;
+  hipLaunchKernelGGL(wq_blocks_kernel, dim3((unsigned)(threads / 256)), dim3(256), 0, s, w, N, K,
+                     ldw, kc, kg, codes, scales, slot);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(wq_finalize_kernel, dim3(1), dim3(1), 0, s, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_weight(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                                uint8_t* codes_rm, uint8_t* scales_rm, hipStream_t s) {
+  const int64_t k_pad = round_up(K, kGroupK);
+  const int kc = (int)(k_pad / kChunkK), kg = (int)(k_pad / kGroupK);
+  const int64_t total = N * (K >> 4);
+  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, codes,
+                     scales, N, K, kc, kg, codes_rm, scales_rm);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((words + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

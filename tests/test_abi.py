@@ -1,0 +1,147 @@
+"""The C ABI library loads, exports every symbol include/nvfp4.h declares,
+and rejects bad arguments on the host before any HIP call.  CPU only: no
+call here reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+LIB = os.path.join(ROOT, "nvfp4_decode_linear_amd", "libnvfp4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnvfp4.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.nvfp4_linear.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                               vp, sz, vp]
+    L.nvfp4_quantize_act.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp]
+    L.nvfp4_quantize_weight.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    L.nvfp4_unpack_weight.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.nvfp4_weight_bytes.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.nvfp4_linear_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
+    L.nvfp4_linear_workspace_bytes.restype = sz
+    L.nvfp4_set_option.argtypes = [ctypes.c_int, i64]
+    L.nvfp4_get_option.argtypes = [ctypes.c_int, ctypes.POINTER(i64)]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_workspace_init.argtypes = [vp, sz, vp]
+    return L
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_versions_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_layout_version() == 1
+    for s in range(6):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_last_hip_error() == 0
+
+
+def test_weight_bytes(lib):
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.nvfp4_weight_bytes(4096, 4096, ctypes.byref(c), ctypes.byref(s)) == 0
+    assert (c.value, s.value) == (4096 * 4096 // 2, 4096 * 4096 // 16)
+    assert lib.nvfp4_weight_bytes(33, 272, ctypes.byref(c), ctypes.byref(s)) == 0
+    assert (c.value, s.value) == (64 * 512 // 2, 64 * 512 // 16)      # padded to 32 x 256
+    assert lib.nvfp4_weight_bytes(16, 24, ctypes.byref(c), ctypes.byref(s)) == 1
+    assert lib.nvfp4_weight_bytes(0, 32, ctypes.byref(c), ctypes.byref(s)) == 1
+    assert lib.nvfp4_weight_bytes(16, 32, None, ctypes.byref(s)) == 1
+
+
+def test_options_roundtrip_and_validation(lib):
+    v = ctypes.c_int64()
+    assert lib.nvfp4_get_option(0, ctypes.byref(v)) == 0 and v.value == 8
+    assert lib.nvfp4_set_option(0, 2) == 0
+    assert lib.nvfp4_get_option(0, ctypes.byref(v)) == 0 and v.value == 2
+    assert lib.nvfp4_set_option(0, 8) == 0
+    assert lib.nvfp4_set_option(0, 9) == 1
+    assert lib.nvfp4_set_option(2, 6) == 1          # chunks per wave must be a multiple of 4
+    assert lib.nvfp4_set_option(3, 2) == 1
+    assert lib.nvfp4_set_option(99, 0) == 2
+    assert lib.nvfp4_get_option(99, ctypes.byref(v)) == 2
+
+
+def test_workspace_bytes(lib):
+    assert lib.nvfp4_linear_workspace_bytes(9, 4096, 4096) == 0
+    assert lib.nvfp4_linear_workspace_bytes(1, 4096, 24) == 0
+    # 8B O projection: 128 row tiles -> split-K is needed to fill 256 CUs.
+    assert lib.nvfp4_linear_workspace_bytes(1, 4096, 4096) > 0
+    # 8B gate_up: enough row tiles without splitting K.
+    assert lib.nvfp4_linear_workspace_bytes(1, 24576, 4096) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture
+def no_gpu():
+    """Calls below pass fake device pointers and expect a host-side error; a
+    validation bug would turn one into a kernel launch, so they only run
+    where no GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+
+
+def test_linear_argument_errors(lib, no_gpu):
+    f = lib.nvfp4_linear
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None)
+    assert f(9, 256, 512, *ok) == 2                           # M > 8: unsupported
+    assert f(0, 256, 512, *ok) == 1
+    assert f(1, 256, 520, *ok) == 1                           # K % 16 != 0
+    assert f(1, 0, 512, *ok) == 1
+    bad = list(ok)
+    bad[0] = None
+    assert f(1, 256, 512, *bad) == 1                          # null x_codes
+    bad = list(ok)
+    bad[7] = 5
+    assert f(1, 256, 512, *bad) == 1                          # unknown output dtype
+    bad = list(ok)
+    bad[8] = ctypes.c_void_p(0x1001)
+    assert f(1, 4096, 4096, *bad) == 1                        # misaligned workspace
+    bad = list(ok)
+    bad[9] = 16
+    assert f(1, 4096, 4096, *bad) == 4                        # workspace too small
+    bad = list(ok)
+    bad[3] = ctypes.c_void_p(0x1008)
+    assert f(1, 256, 512, *bad) == 1                          # misaligned tiled codes
+
+
+def test_quantize_argument_errors(lib, no_gpu):
+    assert lib.nvfp4_quantize_act(FAKE, 9, 512, 512, FAKE, FAKE, FAKE, None) == 2
+    assert lib.nvfp4_quantize_act(FAKE, 1, 520, 520, FAKE, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 500, FAKE, FAKE, FAKE, None) == 1   # ldx < K
+    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 516, FAKE, FAKE, FAKE, None) == 1   # ldx % 8
+    assert lib.nvfp4_quantize_act(None, 1, 512, 512, FAKE, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_quantize_weight(FAKE, 256, 24, 24, FAKE, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_quantize_weight(FAKE, 256, 512, 256, FAKE, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_quantize_weight(ctypes.c_void_p(0x1002), 256, 512, 512, FAKE, FAKE, FAKE,
+                                     None) == 1
+    assert lib.nvfp4_unpack_weight(FAKE, FAKE, 256, 24, FAKE, FAKE, None) == 1
+    assert lib.nvfp4_workspace_init(ctypes.c_void_p(0x1002), 64, None) == 1
+    assert lib.nvfp4_workspace_init(None, 0, None) == 0
+
+
+def test_no_device_is_reported(lib, no_gpu):
+    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 512, FAKE, FAKE, FAKE, None) == 3
+    assert lib.nvfp4_linear(1, 256, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                            1 << 20, None) == 3
