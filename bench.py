@@ -229,9 +229,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1 x e2m1, e4m3 block-16 scales, fp32 accumulate)",
-        "data": "synthetic (seeded; bf16 weights 0.02*N(0,1), activations N(0,1) with 1% x20 "
-                "outlier channels); weights rotated over %d copies (%.2f GiB)"
-                % (copies, copies * set_bytes / (1 << 30)),
+        "data": ("synthetic (seeded; bf16 weights 0.02*N(0,1), activations N(0,1) with 1%% x20 "
+                 "outlier channels); weights rotated over %d copies (%.2f GiB)"
+                 % (copies, copies * set_bytes / (1 << 30))),
         "config": {"workload": f"{wl}_m{M}", "M": M,
                    "linears": [f"{L.name} {L.N}x{L.K}" for L in linears],
                    "path": "per projection: nvfp4_quantize_act + nvfp4_linear (f32 out)"},

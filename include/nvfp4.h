@@ -93,7 +93,14 @@ typedef enum {
                                  of 4).                                     */
   NVFP4_OPT_NONTEMPORAL = 3,  /* 1 (default) = stream weights with
                                  non-temporal loads; 0 = ordinary loads.   */
-  NVFP4_OPT_COUNT = 4
+  NVFP4_OPT_WAVES = 4,        /* 0 = heuristic; else 4, 8 or 16 wavefronts
+                                 per GEMV workgroup (one 32-row tile).     */
+  NVFP4_OPT_KERNEL = 5,       /* 0 = heuristic; 1 = persistent streaming
+                                 GEMV (whole K per workgroup; M <= 3 and the
+                                 activation must fit in LDS, else the split
+                                 kernel runs); 2 = split-K GEMV (one
+                                 workgroup per tile and K slice).           */
+  NVFP4_OPT_COUNT = 6
 } nvfp4_option;
 
 /* ABI version of this header (incremented on any signature change). */
@@ -146,7 +153,10 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
                                 void* stream);
 
 /* Workspace bytes nvfp4_linear needs for this shape under the current
- * options (split-K partial sums and arrival counters).  0 is possible. */
+ * options: 0 when K is not split, else a fixed 64 KiB region of split-K
+ * arrival counters (one per 32-row tile) followed by the binary32 partial
+ * sums [splits][M][N_pad].  Because the counters sit at the same place for
+ * every shape, one workspace sized for the largest shape serves all. */
 size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K);
 
 /* Zero a workspace before its first use (a fill kernel on `stream`).  The
@@ -156,7 +166,7 @@ size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K);
 nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* The decode linear y[m][n] = xgs * wgs * sum_k x[m][k] w[n][k] over the
- * dequantized NVFP4 operands, 1 <= M <= 8.
+ * dequantized NVFP4 operands, 1 <= M <= 8, N <= 524288.
  *   x_codes/x_scales canonical activation ([M][K/2], [M][K/16]); x_gscale
  *   and w_gscale device floats; w_codes/w_scales device-tiled weight;
  *   y [M][N] row-major, binary32 or bf16 (round to nearest even);

@@ -22,7 +22,7 @@ constexpr int kLayoutVersion = 1;
 constexpr int kMaxM = 8;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{8}, {0}, {0}, {1}};
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{8}, {0}, {0}, {1}, {0}, {0}};
 thread_local int t_last_hip = 0;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -59,41 +59,97 @@ bool valid_nk(int64_t N, int64_t K) {
          round_up(N, nvfp4::kTileN) * round_up(K, nvfp4::kGroupK) / 2 <= (int64_t(1) << 40);
 }
 
+// LDS bytes of one split-kernel workgroup: the decoded activation slice (M
+// rows x cps chunks x 64 f16) plus the cross-wave reduction buffer.
+int64_t split_lds_bytes(int M, int cpw, int waves) {
+  return (int64_t)M * cpw * waves * 128 + (int64_t)waves * M * 128 + 64;
+}
+
+bool split_ok(int M, int cpw, int waves) {
+  if (waves == 16 && cpw > 8) return false;      // 1024 threads: <= 128 VGPRs per lane
+  return split_lds_bytes(M, cpw, waves) <= 65536;
+}
+
+// LDS bytes of one stream-kernel workgroup: the whole decoded activation (M
+// rows x kc chunks x 64 f16) plus the double-buffered reduction array.
+int64_t stream_lds_bytes(int M, int kc, int waves) {
+  return (int64_t)M * kc * 128 + 2 * (int64_t)waves * M * 128;
+}
+
+constexpr int64_t kLdsBudget = 160 * 1024;
+
+void finish_workspace(GemvPlan& p, int M) {
+  // The arrival counters live in a fixed region at the start of the
+  // workspace, so one zero-initialised workspace stays valid across calls of
+  // any shape (a counter never lands where another shape left partial sums).
+  const int64_t n_pad = (int64_t)p.tiles * nvfp4::kTileN;
+  p.ws_partials = p.splits > 1 ? (size_t)round_up((int64_t)p.splits * M * n_pad * 4, 256) : 0;
+  p.ws_bytes = p.splits > 1 ? nvfp4::kCounterBytes + p.ws_partials : 0;
+}
+
 // Launch plan of the VALU GEMV for (M, N, K) under the current knobs.
 GemvPlan make_plan(int M, int64_t N, int64_t K) {
   GemvPlan p;
   p.kc = (int)(round_up(K, nvfp4::kGroupK) / nvfp4::kChunkK);
   p.tiles = (int)(round_up(N, nvfp4::kTileN) / nvfp4::kTileN);
-  p.waves = 4;
   p.nontemporal = g_opts[NVFP4_OPT_NONTEMPORAL].load() ? 1 : 0;
+  const int64_t force_kernel = g_opts[NVFP4_OPT_KERNEL].load();
   const int64_t force_cpw = g_opts[NVFP4_OPT_CHUNKS_PER_WAVE].load();
   const int64_t force_split = g_opts[NVFP4_OPT_SPLIT_K].load();
-  // Enough workgroups to give every one of the 256 CUs two, with each
-  // wavefront streaming as many 1 KiB records as possible (<= 16).
-  const int64_t want_wgs = 512;
+  const int64_t force_waves = g_opts[NVFP4_OPT_WAVES].load();
+
+  // Stream kernel: one workgroup per CU walks whole row tiles (all of K), so
+  // no split-K reduction is needed; it needs the whole activation in LDS.
+  // Waves per workgroup = ceil(kc / cpw) <= 16 so that every wave has work.
+  const bool use_stream = M <= 3 && (force_kernel == 1 || (force_kernel == 0 && force_split == 0 &&
+                                                           force_cpw == 0));
+  if (use_stream) {
+    const int max_waves = M == 1 ? 16 : 8;                    // as compiled
+    const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves) : max_waves;
+    const int cpw = (int)round_up((p.kc + want - 1) / want, 4);
+    const int waves = (p.kc + cpw - 1) / cpw;
+    if (waves <= max_waves && stream_lds_bytes(M, p.kc, waves) <= kLdsBudget) {
+      p.kind = nvfp4::kGemvStream;
+      p.waves = waves;
+      p.depth = 8;
+      p.cpw = cpw;
+      p.cps = cpw * waves;
+      p.splits = 1;
+      // one resident workgroup per CU (the launch reserves enough LDS)
+      p.grid = std::min(p.tiles, 256);
+      finish_workspace(p, M);
+      return p;
+    }
+  }
+
+  // Split kernel: one workgroup per (row tile, K slice).
+  p.kind = nvfp4::kGemvSplit;
+  p.depth = 0;
+  int waves = force_waves > 0 ? (int)force_waves : 4;
   int cpw = 4;
   if (force_cpw > 0) {
     cpw = (int)force_cpw;
   } else if (force_split > 0) {
     const int64_t per = (p.kc + force_split - 1) / force_split;          // chunks per slice
-    cpw = (int)std::min<int64_t>(16, std::max<int64_t>(4, round_up((per + 3) / 4, 4)));
+    cpw = (int)std::min<int64_t>(16, std::max<int64_t>(4, round_up((per + waves - 1) / waves, 4)));
   } else {
+    // Enough workgroups to give every one of the 256 CUs two, with each
+    // wavefront streaming as many 1 KiB records as possible (<= 16).
+    const int64_t want_wgs = 512;
     const int cands[4] = {16, 12, 8, 4};
     for (int c : cands) {
-      const int64_t splits = (p.kc + 4 * c - 1) / (4 * c);
+      const int64_t splits = (p.kc + (int64_t)waves * c - 1) / ((int64_t)waves * c);
       if ((int64_t)p.tiles * splits >= want_wgs) { cpw = c; break; }
     }
   }
-  // LDS per workgroup: the decoded activation slice (M * cps * 64 f16) plus
-  // the cross-wave reduction buffer; kept within 64 KiB.
-  while (cpw > 4 && (int64_t)M * cpw * p.waves * 128 + (int64_t)p.waves * M * 128 + 64 > 65536)
-    cpw -= 4;
+  while (cpw > 4 && !split_ok(M, cpw, waves)) cpw -= 4;
+  while (waves > 4 && !split_ok(M, cpw, waves)) waves /= 2;
+  p.waves = waves;
   p.cpw = cpw;
   p.cps = cpw * p.waves;
   p.splits = (p.kc + p.cps - 1) / p.cps;
-  const int64_t n_pad = (int64_t)p.tiles * nvfp4::kTileN;
-  p.ws_partials = p.splits > 1 ? (size_t)round_up((int64_t)p.splits * M * n_pad * 4, 256) : 0;
-  p.ws_bytes = p.splits > 1 ? p.ws_partials + (size_t)round_up((int64_t)p.tiles * 4, 256) : 0;
+  p.grid = p.tiles * p.splits;
+  finish_workspace(p, M);
   return p;
 }
 
@@ -130,6 +186,12 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
       break;
     case NVFP4_OPT_NONTEMPORAL:
       if (value != 0 && value != 1) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_WAVES:
+      if (value != 0 && value != 4 && value != 8 && value != 16) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_KERNEL:
+      if (value < 0 || value > 2) return NVFP4_ERR_INVALID_ARG;
       break;
     default: return NVFP4_ERR_UNSUPPORTED;
   }
@@ -194,7 +256,9 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
 }
 
 size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {
-  if (M < 1 || M > kMaxM || !valid_nk(N, K)) return 0;
+  if (M < 1 || M > kMaxM || !valid_nk(N, K) ||
+      N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN)
+    return 0;
   return make_plan(M, N, K).ws_bytes;
 }
 
@@ -211,7 +275,8 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
                           const uint8_t* w_scales, const float* w_gscale, void* y, int out_dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
   if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
-  if (M < 1 || !valid_nk(N, K) || N > (int64_t(1) << 28) || K > (int64_t(1) << 28))
+  if (M < 1 || !valid_nk(N, K) || N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
+      K > (int64_t(1) << 28))
     return NVFP4_ERR_INVALID_ARG;
   if (!x_codes || !x_scales || !x_gscale || !w_codes || !w_scales || !w_gscale || !y)
     return NVFP4_ERR_INVALID_ARG;
@@ -225,9 +290,12 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
     if (workspace_bytes < p.ws_bytes) return NVFP4_ERR_WORKSPACE;
   }
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
-  const hipError_t e = nvfp4::launch_gemv_valu(p, M, N, K, x_codes, x_scales, x_gscale, w_codes,
-                                               w_scales, w_gscale, y, out_dtype, workspace,
-                                               (hipStream_t)stream);
+  const hipError_t e =
+      p.kind == nvfp4::kGemvStream
+          ? nvfp4::launch_gemv_stream(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,
+                                      w_gscale, y, out_dtype, (hipStream_t)stream)
+          : nvfp4::launch_gemv_split(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,
+                                     w_gscale, y, out_dtype, workspace, (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 

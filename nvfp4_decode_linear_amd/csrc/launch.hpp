@@ -9,16 +9,27 @@
 
 namespace nvfp4 {
 
+// Split-K arrival counters: one per row tile, in a fixed region at the start
+// of every workspace.  Shapes with more row tiles never split K.
+constexpr int kMaxCounterTiles = 16384;
+constexpr size_t kCounterBytes = (size_t)kMaxCounterTiles * 4;
+
+enum GemvKind { kGemvStream = 0, kGemvSplit = 1 };
+
 struct GemvPlan {
+  int kind;      // kGemvStream: persistent, whole K per workgroup, no workspace
+                 // kGemvSplit: one workgroup per (tile, K slice), split-K tail
   int kc;        // K_pad / 64 chunks
   int tiles;     // N_pad / 32 row tiles
-  int cpw;       // chunks per wavefront (multiple of 4)
+  int cpw;       // chunks per wavefront (per tile and slice; multiple of 4)
   int waves;     // wavefronts per workgroup
-  int cps;       // chunks per K slice (= cpw * waves)
-  int splits;    // K slices
+  int cps;       // chunks per K slice (= cpw * waves; split kernel)
+  int splits;    // K slices (split kernel; 1 for the stream kernel)
+  int depth;     // weight records in flight per wavefront (stream kernel)
+  int grid;      // workgroups launched
   int nontemporal;
-  size_t ws_partials;  // bytes of split-K partials in the workspace
-  size_t ws_bytes;     // total workspace bytes
+  size_t ws_partials;  // bytes of split-K partials (after the counter region)
+  size_t ws_bytes;     // total workspace bytes (0 without split-K)
 };
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -34,9 +45,14 @@ hipError_t launch_unpack_weight(const uint8_t* codes, const uint8_t* scales, int
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
-hipError_t launch_gemv_valu(const GemvPlan& p, int M, int64_t N, int64_t K,
-                            const uint8_t* xc, const uint8_t* xs, const float* xg,
-                            const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,
-                            int out_bf16, void* workspace, hipStream_t s);
+hipError_t launch_gemv_split(const GemvPlan& p, int M, int64_t N, int64_t K,
+                             const uint8_t* xc, const uint8_t* xs, const float* xg,
+                             const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,
+                             int out_bf16, void* workspace, hipStream_t s);
+
+hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
+                              const uint8_t* xc, const uint8_t* xs, const float* xg,
+                              const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,
+                              int out_bf16, hipStream_t s);
 
 }  // namespace nvfp4

@@ -36,12 +36,36 @@ __device__ inline uint32_t absmax_bits(const uint32_t (&v)[8]) {
 
 // ------------------------------------------------------------ activations
 //
-// One workgroup quantizes the whole M x K activation: pass 1 takes the
-// tensor amax (bf16 magnitudes compared as integers, exact), pass 2
-// re-reads each 16-block (an L2 hit) and writes its scale and codes.  The
-// tensor scale never leaves the device.
+// One workgroup quantizes the whole M x K activation.  The tensor amax is a
+// reduction over every element (bf16 magnitudes compared as integers, exact)
+// and must be known before any block can be scaled.  When the tensor has at
+// most 4 blocks of 16 per thread (BPT > 0) each thread keeps its blocks in
+// registers between the reduction and the quantization; otherwise (BPT == 0)
+// the second pass re-reads the blocks (an L2 hit).  The tensor scale never
+// leaves the device.
 constexpr int kActThreads = 1024;
+constexpr int kActBpt = 4;
 
+__device__ inline uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t all = 0;
+#pragma unroll
+  for (int w = 0; w < kActThreads / kWave; ++w) all = max(all, red[w]);
+  return all;
+}
+
+__device__ inline void store_block(uint8_t* codes, uint8_t* scales, int K, int m, int j,
+                                   const BlockQ& q) {
+  u32x2 c;
+  c.x = q.lo;
+  c.y = q.hi;
+  *reinterpret_cast<u32x2*>(codes + (int64_t)m * (K >> 1) + 8 * j) = c;
+  scales[(int64_t)m * (K >> 4) + j] = (uint8_t)q.scale;
+}
+
+template <int BPT>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ gscale) {
@@ -49,30 +73,44 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   const int nbr = K >> 4;
   const int nb = M * nbr;
   uint32_t amax = 0;
-  for (int b = threadIdx.x; b < nb; b += kActThreads) {
-    const int m = b / nbr, j = b - m * nbr;
-    uint32_t v[8];
-    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
-    amax = max(amax, absmax_bits(v));
-  }
-  amax = wave_max_u32(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  uint32_t all = 0;
+  if constexpr (BPT > 0) {
+    uint32_t v[BPT][8];
 #pragma unroll
-  for (int w = 0; w < kActThreads / kWave; ++w) all = max(all, red[w]);
-  const float sg = tensor_scale(bf16_to_f32(all));
-  if (threadIdx.x == 0) *gscale = sg;
-  for (int b = threadIdx.x; b < nb; b += kActThreads) {
-    const int m = b / nbr, j = b - m * nbr;
-    uint32_t v[8];
-    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
-    const BlockQ q = quantize_block_bf16(v, sg);
-    u32x2 c;
-    c.x = q.lo;
-    c.y = q.hi;
-    *reinterpret_cast<u32x2*>(codes + (int64_t)m * (K >> 1) + 8 * j) = c;
-    scales[(int64_t)m * nbr + j] = (uint8_t)q.scale;
+    for (int r = 0; r < BPT; ++r) {
+      const int b = threadIdx.x + r * kActThreads;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[r][i] = 0u;
+      if (b < nb) {
+        const int m = b / nbr, j = b - m * nbr;
+        load_block_bf16(x + (int64_t)m * ldx + 16 * j, v[r]);
+      }
+      amax = max(amax, absmax_bits(v[r]));
+    }
+    const float sg = tensor_scale(bf16_to_f32(block_reduce_max(amax, red)));
+    if (threadIdx.x == 0) *gscale = sg;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int b = threadIdx.x + r * kActThreads;
+      if (b < nb) {
+        const int m = b / nbr, j = b - m * nbr;
+        store_block(codes, scales, K, m, j, quantize_block_bf16(v[r], sg));
+      }
+    }
+  } else {
+    for (int b = threadIdx.x; b < nb; b += kActThreads) {
+      const int m = b / nbr, j = b - m * nbr;
+      uint32_t v[8];
+      load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
+      amax = max(amax, absmax_bits(v));
+    }
+    const float sg = tensor_scale(bf16_to_f32(block_reduce_max(amax, red)));
+    if (threadIdx.x == 0) *gscale = sg;
+    for (int b = threadIdx.x; b < nb; b += kActThreads) {
+      const int m = b / nbr, j = b - m * nbr;
+      uint32_t v[8];
+      load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
+      store_block(codes, scales, K, m, j, quantize_block_bf16(v, sg));
+    }
   }
 }
 
@@ -176,8 +214,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t word
 
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
                                uint8_t* scales, float* gscale, hipStream_t s) {
-  hipLaunchKernelGGL(act_quant_kernel, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx, codes,
-                     scales, gscale);
+  if ((int64_t)M * (K >> 4) <= (int64_t)kActThreads * kActBpt)
+    hipLaunchKernelGGL(act_quant_kernel<kActBpt>, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx,
+                       codes, scales, gscale);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<0>, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx, codes,
+                       scales, gscale);
   return hipGetLastError();
 }
 

@@ -83,10 +83,18 @@ def test_options_roundtrip_and_validation(lib):
 def test_workspace_bytes(lib):
     assert lib.nvfp4_linear_workspace_bytes(9, 4096, 4096) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 4096, 24) == 0
-    # 8B O projection: 128 row tiles -> split-K is needed to fill 256 CUs.
-    assert lib.nvfp4_linear_workspace_bytes(1, 4096, 4096) > 0
-    # 8B gate_up: enough row tiles without splitting K.
-    assert lib.nvfp4_linear_workspace_bytes(1, 24576, 4096) == 0
+    # The streaming kernel (the default whenever the activation fits in LDS)
+    # needs no workspace.
+    assert lib.nvfp4_linear_workspace_bytes(1, 4096, 4096) == 0
+    assert lib.nvfp4_linear_workspace_bytes(8, 5120, 25600) > 0      # too big for LDS: split-K
+    # Forcing the split-K kernel on the 8B O projection needs one: 64 KiB of
+    # counters plus [splits][M][N] partial sums.
+    assert lib.nvfp4_set_option(5, 2) == 0
+    try:
+        n = lib.nvfp4_linear_workspace_bytes(1, 4096, 4096)
+        assert n > 64 * 1024 and (n - 64 * 1024) % (4096 * 4) == 0
+    finally:
+        assert lib.nvfp4_set_option(5, 0) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)
@@ -115,12 +123,14 @@ def test_linear_argument_errors(lib, no_gpu):
     bad = list(ok)
     bad[7] = 5
     assert f(1, 256, 512, *bad) == 1                          # unknown output dtype
+    # (8, 5120, 25600): too large for the streaming kernel, so split-K with a
+    # workspace
     bad = list(ok)
     bad[8] = ctypes.c_void_p(0x1001)
-    assert f(1, 4096, 4096, *bad) == 1                        # misaligned workspace
+    assert f(8, 5120, 25600, *bad) == 1                       # misaligned workspace
     bad = list(ok)
     bad[9] = 16
-    assert f(1, 4096, 4096, *bad) == 4                        # workspace too small
+    assert f(8, 5120, 25600, *bad) == 4                       # workspace too small
     bad = list(ok)
     bad[3] = ctypes.c_void_p(0x1008)
     assert f(1, 256, 512, *bad) == 1                          # misaligned tiled codes

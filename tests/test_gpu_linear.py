@@ -27,7 +27,8 @@ def nv():
         pytest.fail("GPU tests need a visible GPU")
     import nvfp4_decode_linear_amd as nv
     yield nv
-    for k, v in (("split_k", 0), ("chunks_per_wave", 0), ("nontemporal", 1), ("gemv_max_m", 8)):
+    for k, v in (("split_k", 0), ("chunks_per_wave", 0), ("nontemporal", 1), ("gemv_max_m", 8),
+                 ("waves", 0), ("kernel", 0)):
         nv.set_option(k, v)
 
 
@@ -206,22 +207,30 @@ def test_run_to_run_bit_stable(nv):
         assert np.array_equal(y.numpy().view(np.uint32), ys[0].numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("split,cpw", [(1, 0), (2, 0), (3, 0), (7, 0), (0, 4), (0, 8), (0, 12),
-                                       (0, 16)])
-def test_knobs_keep_results_in_tolerance(nv, split, cpw):
-    L = QWEN3_8B[1]
-    note(f"linear knobs split_k={split} chunks_per_wave={cpw}")
+KNOBS = [  # (kernel, split_k, chunks_per_wave, waves)
+    (2, 1, 0, 0), (2, 2, 0, 0), (2, 3, 0, 0), (2, 7, 0, 0), (2, 0, 4, 0), (2, 0, 8, 0),
+    (2, 0, 12, 0), (2, 0, 16, 0), (2, 0, 4, 8), (2, 0, 16, 8), (2, 0, 4, 16), (2, 0, 8, 16),
+    (2, 2, 0, 16), (1, 0, 0, 0), (1, 0, 0, 8), (1, 0, 0, 16),
+]
+
+
+@pytest.mark.parametrize("kernel,split,cpw,waves", KNOBS)
+def test_knobs_keep_results_in_tolerance(nv, kernel, split, cpw, waves):
+    L = QWEN3_8B[3]
+    note(f"linear knobs kernel={kernel} split_k={split} chunks_per_wave={cpw} waves={waves}")
+    nv.set_option("kernel", kernel)
     nv.set_option("split_k", split)
     nv.set_option("chunks_per_wave", cpw)
+    nv.set_option("waves", waves)
     try:
-        for M in (1, 8):
-            w16, x16, wq, xq = _quantized_pair(nv, 3, 1, L, M, "outlier")
+        for M in (1, 3, 8):
+            w16, x16, wq, xq = _quantized_pair(nv, 3, 3, L, M, "outlier")
             y = nv.linear(xq, wq)
             _sync()
             _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(2), 128))
     finally:
-        nv.set_option("split_k", 0)
-        nv.set_option("chunks_per_wave", 0)
+        for k in ("kernel", "split_k", "chunks_per_wave", "waves"):
+            nv.set_option(k, 0)
 
 
 def test_ordinary_loads_match_nontemporal(nv):
@@ -269,3 +278,21 @@ def test_graph_replay_matches_eager(nv):
         assert np.array_equal(y.cpu().numpy().view(np.uint32), eager.cpu().numpy().view(np.uint32)), i
         nv.linear(xq, wq, out=y, ws=ws)          # eager call between replays
         _sync()
+
+
+def test_workspace_shared_across_shapes(nv):
+    """One zero-initialised workspace serves calls of different shapes in any
+    order: the split-K counters sit in a fixed region, so a small shape never
+    reads a larger shape's partial sums as counters."""
+    import torch
+    shapes = [(5120, 8192, 1), (100, 1040, 1), (4096, 12288, 8), (33, 784, 3), (4096, 4096, 2)]
+    need = max(nv.linear_workspace_bytes(M, N, K) for N, K, M in shapes)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    nv.workspace_init(ws)
+    for rep in range(2):
+        for N, K, M in shapes:
+            note(f"shared workspace rep={rep} M={M} N={N} K={K}")
+            xq, wq, ox, ow = _unit_operands(nv, M, N, K, seed=N + K + M)
+            y = nv.linear(xq, wq, ws=ws)
+            _sync()
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.linear_ref(ox, ow))
