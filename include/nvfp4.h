@@ -86,7 +86,7 @@ typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
  * benchmarks", the Python wiring example). */
 typedef enum {
   NVFP4_OPT_GEMV_MAX_M = 0,   /* M <= value uses the VALU GEMV; larger M uses
-                                 the MFMA skinny GEMM.  Default 8; 0..8.   */
+                                 the FP4 MFMA GEMM.  0..8.                 */
   NVFP4_OPT_SPLIT_K = 1,      /* 0 = heuristic; s >= 1 forces s K-slices.  */
   NVFP4_OPT_CHUNKS_PER_WAVE = 2, /* 0 = heuristic; else 64-element K chunks
                                  each wavefront streams per row tile (multiple
@@ -96,10 +96,13 @@ typedef enum {
   NVFP4_OPT_WAVES = 4,        /* 0 = heuristic; else 4, 8 or 16 wavefronts
                                  per GEMV workgroup (one 32-row tile).     */
   NVFP4_OPT_KERNEL = 5,       /* 0 = heuristic; 1 = persistent streaming
-                                 GEMV (whole K per workgroup; M <= 3 and the
-                                 activation must fit in LDS, else the split
-                                 kernel runs); 2 = split-K GEMV (one
-                                 workgroup per tile and K slice).           */
+                                 VALU GEMV (whole K per workgroup; M <= 3
+                                 and the activation must fit in LDS, else
+                                 the split kernel runs); 2 = split-K VALU
+                                 GEMV (one workgroup per tile and K slice);
+                                 3 = persistent streaming GEMV with the dot
+                                 on FP4 MFMA (falls back to split-K when the
+                                 activation does not fit in LDS).          */
   NVFP4_OPT_COUNT = 6
 } nvfp4_option;
 

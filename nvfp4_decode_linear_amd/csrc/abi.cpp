@@ -70,12 +70,6 @@ bool split_ok(int M, int cpw, int waves) {
   return split_lds_bytes(M, cpw, waves) <= 65536;
 }
 
-// LDS bytes of one stream-kernel workgroup: the whole decoded activation (M
-// rows x kc chunks x 64 f16) plus the double-buffered reduction array.
-int64_t stream_lds_bytes(int M, int kc, int waves) {
-  return (int64_t)M * kc * 128 + 2 * (int64_t)waves * M * 128;
-}
-
 constexpr int64_t kLdsBudget = 160 * 1024;
 
 void finish_workspace(GemvPlan& p, int M) {
@@ -98,20 +92,24 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
   const int64_t force_split = g_opts[NVFP4_OPT_SPLIT_K].load();
   const int64_t force_waves = g_opts[NVFP4_OPT_WAVES].load();
 
-  // Stream kernel: one workgroup per CU walks whole row tiles (all of K), so
-  // no split-K reduction is needed; it needs the whole activation in LDS.
-  // Waves per workgroup = ceil(kc / cpw) <= 16 so that every wave has work.
-  const bool use_stream = M <= 3 && (force_kernel == 1 || (force_kernel == 0 && force_split == 0 &&
-                                                           force_cpw == 0));
-  if (use_stream) {
-    const int max_waves = M == 1 ? 16 : 8;                    // as compiled
+  // Streaming kernels: one workgroup per CU walks whole row tiles (all of
+  // K), so no split-K reduction is needed; they need the whole activation in
+  // LDS.  Waves per workgroup = ceil(kc / cpw) so that every wave has work.
+  // M <= GEMV_MAX_M runs the VALU dot (M <= 3 only), larger M the MFMA dot.
+  const int64_t gemv_max_m = g_opts[NVFP4_OPT_GEMV_MAX_M].load();
+  const bool auto_kind = force_kernel == 0 && force_split == 0 && force_cpw == 0;
+  const bool want_mfma = force_kernel == 3 || (auto_kind && (M > gemv_max_m || M > 3));
+  const bool want_valu = !want_mfma && (force_kernel == 1 || auto_kind) && M <= 3;
+  if (want_mfma || want_valu) {
+    const int max_waves = want_mfma ? (M <= 3 ? 16 : 8) : (M == 1 ? 16 : 8);  // as compiled
     const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves) : max_waves;
     const int cpw = (int)round_up((p.kc + want - 1) / want, 4);
     const int waves = (p.kc + cpw - 1) / cpw;
-    if (waves <= max_waves && stream_lds_bytes(M, p.kc, waves) <= kLdsBudget) {
-      p.kind = nvfp4::kGemvStream;
+    if (waves <= max_waves &&
+        (int64_t)nvfp4::stream_lds_need(M, p.kc, waves, want_mfma) <= kLdsBudget) {
+      p.kind = want_mfma ? nvfp4::kGemvMfma : nvfp4::kGemvStream;
       p.waves = waves;
-      p.depth = 8;
+      p.depth = 12;
       p.cpw = cpw;
       p.cps = cpw * waves;
       p.splits = 1;
@@ -191,7 +189,7 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
       if (value != 0 && value != 4 && value != 8 && value != 16) return NVFP4_ERR_INVALID_ARG;
       break;
     case NVFP4_OPT_KERNEL:
-      if (value < 0 || value > 2) return NVFP4_ERR_INVALID_ARG;
+      if (value < 0 || value > 3) return NVFP4_ERR_INVALID_ARG;
       break;
     default: return NVFP4_ERR_UNSUPPORTED;
   }
@@ -291,7 +289,7 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
   }
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
   const hipError_t e =
-      p.kind == nvfp4::kGemvStream
+      p.kind != nvfp4::kGemvSplit
           ? nvfp4::launch_gemv_stream(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,
                                       w_gscale, y, out_dtype, (hipStream_t)stream)
           : nvfp4::launch_gemv_split(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,

@@ -42,6 +42,10 @@ constexpr int stream_max_waves(int M) { return M == 1 ? 16 : 8; }
 // Groups of 4 weight records (4 KiB) each wave keeps in flight.
 constexpr int stream_ring_groups(int M) { return M == 3 ? 2 : 3; }
 
+// The MFMA variant keeps 16 result registers per chunk but decodes nothing.
+constexpr int mfma_max_waves(int M) { return M <= 3 ? 16 : 8; }
+constexpr int mfma_ring_groups(int) { return 3; }
+
 // The grid holds at most one workgroup per CU.  The hardware dispatcher
 // packs workgroups onto a CU while its registers and LDS last, so every
 // workgroup reserves more than half of the CU's 160 KiB LDS: then no CU can
@@ -56,7 +60,7 @@ using ic = std::integral_constant<int, V>;
 // compile-time constants on every path (the paths never merge), so the
 // compiler's memory wait counts stay exact: where paths with different
 // numbers of outstanding loads merge, it waits for all of them.
-template <int M, int RG>
+template <int M, int RG, bool MF>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -65,8 +69,13 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const bool nt = a.nontemporal != 0;
   const int kc = a.kc;
   const int row_dw = kc * 32;
+  // VALU: x~ as f16 pairs [M][kc * 32 dwords].  MFMA: raw activation codes
+  // [M][kc * 4 blocks][2 dwords], then the E4M3 activation scales as floats
+  // [kc * 4 blocks][M].  Either is followed by the reduction array
+  // [2][NW][M][32] floats.
   uint32_t* xlds = lds;
-  float* red = reinterpret_cast<float*>(lds + M * row_dw);    // [2][NW][M][32]
+  float* sa = reinterpret_cast<float*>(lds + M * kc * 8);
+  float* red = reinterpret_cast<float*>(MF ? lds + M * kc * 8 + kc * 4 * M : lds + M * row_dw);
   const int kb_row = a.K >> 4;
   const int nblk = M * kc * 4;                // activation 16-blocks, padded K
   const int cpw = a.cpw;                      // chunks per wave per tile, multiple of 4
@@ -122,12 +131,21 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // ---- 3. activation into LDS: the first batch from registers, any rest
   // (large M * K only) read now.
   auto prologue = [&]() __attribute__((always_inline)) {
+    auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
+      if constexpr (MF) {
+        xlds[(m * kc * 4 + kb) * 2] = c.x;
+        xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
+        sa[kb * M + m] = e4m3_to_f32(sc);
+      } else {
+        decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
+      }
+    };
 #pragma unroll
     for (int r = 0; r < kStreamXpt; ++r) {
       const int i = threadIdx.x + r * 64 * NW;
       if (i < nblk) {
         const int m = i / (kc * 4), kb = i - m * (kc * 4);
-        decode_act_block(xc[r], xs[r], xlds + m * row_dw + kb * 8);
+        put(m, kb, xc[r], xs[r]);
       }
     }
     for (int i = threadIdx.x + kStreamXpt * 64 * NW; i < nblk; i += 64 * NW) {
@@ -138,7 +156,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         c = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
         sc = a.xs[(int64_t)m * kb_row + kb];
       }
-      decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
+      put(m, kb, c, sc);
     }
     __syncthreads();
   };
@@ -174,6 +192,21 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // Consume ring group q: chunks coff .. coff + 3 of the current tile.  Branch
   // free (wait counts stay exact): a chunk past K (last wave only) reads a
   // valid activation chunk and gets a zero block scale, so it adds exactly 0.
+  // MFMA A operand: lane l holds row r = l % 32 of the 32 x 64 block-diagonal
+  // activation tile, K half l / 32.  Row r is activation row ma, block ja of
+  // the chunk, chosen so that the 32 x 32 result lands with every lane
+  // holding its own weight row n = l % 32 and its own two blocks 2h, 2h + 1
+  // (result v = 4i + q of lane l is tile row 8i + 4h + q = (m 2i + q / 2,
+  // block 2h + q % 2)).  The lane's 16 A bytes are the block's 8 code bytes,
+  // in the low or high half, or zero when the block lies in the other K half
+  // (or the row is past M).
+  const int ra = lane & 31;
+  const int ma = 2 * (ra >> 3) + ((ra & 3) >> 1);
+  const int ja = 2 * ((ra >> 2) & 1) + (ra & 1);
+  const bool a_on = (h == ((ra >> 2) & 1)) && (ma < M);
+  const bool a_lo = a_on && (ra & 1) == 0, a_hi = a_on && (ra & 1) != 0;
+  const uint32_t* xa_row = xlds + (ma < M ? ma : 0) * kc * 8 + ja * 2;
+
   int coff = 0;
   auto consume = [&](auto Q) __attribute__((always_inline)) {
     constexpr int q = decltype(Q)::value;
@@ -183,7 +216,28 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       uint32_t sb = (k < 2 ? rsc[q].x : rsc[q].y) >> (16 * (k & 1));
       sb = c < kc ? sb : 0u;
       const int cx = min(c, kc - 1);
-      dot_chunk<M>(ring[q][k], sb, xlds + ((cx * 64 + 32 * h) >> 1), row_dw, acc);
+      if constexpr (MF) {
+        const uint32_t* xp = xa_row + cx * 8;
+        const uint32_t a0 = xp[0], a1 = xp[1];
+        const v8i A = {(int)(a_lo ? a0 : 0u), (int)(a_lo ? a1 : 0u), (int)(a_hi ? a0 : 0u),
+                       (int)(a_hi ? a1 : 0u), 0, 0, 0, 0};
+        const u32x4 wv = ring[q][k];
+        const v8i B = {(int)wv.x, (int)wv.y, (int)wv.z, (int)wv.w, 0, 0, 0, 0};
+        const v16f C = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, v16f{}, 4, 4, 0, 127,
+                                                                       0, 127);
+        const float sw0 = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
+        const float sw1 = __builtin_amdgcn_cvt_f32_fp8(sb, 1);
+        const float* sap = sa + (4 * cx + 2 * h) * M;          // [block 2h + b][m]
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 2 * (v >> 2) + ((v & 3) >> 1), b = v & 1;
+          if constexpr (true) {
+            if (m < M) acc[m] = fmaf(C[v], sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
+          }
+        }
+      } else {
+        dot_chunk<M>(ring[q][k], sb, xlds + ((cx * 64 + 32 * h) >> 1), row_dw, acc);
+      }
     }
     coff += 4;
     if (coff == cpw) {
@@ -261,21 +315,35 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 template <int M>
 __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, stream_ring_groups(M)>(a, lds);
+  stream_body<M, stream_ring_groups(M), false>(a, lds);
 }
 
 template <int M>
+__global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
+  extern __shared__ uint32_t lds[];
+  stream_body<M, mfma_ring_groups(M), true>(a, lds);
+}
+
+template <int M, bool MF>
 hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  if (p.waves < 1 || p.waves > stream_max_waves(M)) return hipErrorInvalidValue;
-  const size_t need = (size_t)M * p.kc * 64 * sizeof(uint16_t) +
-                      (size_t)2 * p.waves * M * 32 * sizeof(float);
+  if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
+    return hipErrorInvalidValue;
+  const size_t need = stream_lds_need(M, p.kc, p.waves, MF);
   const size_t lds = need > kStreamLdsReserve ? need : kStreamLdsReserve;
-  static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemv_stream_kernel<M>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  const void* fn;
+  if constexpr (MF)
+    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M>);
+  else
+    fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M>);
+  static hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemv_stream_kernel<M>), dim3((unsigned)p.grid), dim3(64 * p.waves), lds, s,
-                     a);
+  if constexpr (MF)
+    hipLaunchKernelGGL((gemv_mfma_kernel<M>), dim3((unsigned)p.grid), dim3(64 * p.waves), lds, s,
+                       a);
+  else
+    hipLaunchKernelGGL((gemv_stream_kernel<M>), dim3((unsigned)p.grid), dim3(64 * p.waves), lds,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -303,11 +371,24 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
   a.out_bf16 = out_bf16;
   a.nontemporal = p.nontemporal;
   a.tiles = p.tiles;
+  if (p.kind == kGemvMfma) {
+    switch (M) {
+      case 1: return launch_m<1, true>(p, a, s);
+      case 2: return launch_m<2, true>(p, a, s);
+      case 3: return launch_m<3, true>(p, a, s);
+      case 4: return launch_m<4, true>(p, a, s);
+      case 5: return launch_m<5, true>(p, a, s);
+      case 6: return launch_m<6, true>(p, a, s);
+      case 7: return launch_m<7, true>(p, a, s);
+      case 8: return launch_m<8, true>(p, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   static_assert(kStreamMaxM == 3, "one case per supported row count");
   switch (M) {
-    case 1: return launch_m<1>(p, a, s);
-    case 2: return launch_m<2>(p, a, s);
-    case 3: return launch_m<3>(p, a, s);
+    case 1: return launch_m<1, false>(p, a, s);
+    case 2: return launch_m<2, false>(p, a, s);
+    case 3: return launch_m<3, false>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }

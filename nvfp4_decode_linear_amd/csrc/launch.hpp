@@ -14,10 +14,19 @@ namespace nvfp4 {
 constexpr int kMaxCounterTiles = 16384;
 constexpr size_t kCounterBytes = (size_t)kMaxCounterTiles * 4;
 
-enum GemvKind { kGemvStream = 0, kGemvSplit = 1 };
+enum GemvKind { kGemvStream = 0, kGemvSplit = 1, kGemvMfma = 2 };
+
+// Dynamic LDS bytes of a streaming workgroup (VALU or MFMA variant) with
+// `waves` wavefronts, before the reservation that keeps one workgroup per CU.
+inline size_t stream_lds_need(int M, int kc, int waves, bool mfma) {
+  const size_t act = mfma ? (size_t)M * kc * 32 + (size_t)kc * 4 * M * 4   // codes + scales
+                          : (size_t)M * kc * 128;                          // f16 x~
+  return act + (size_t)2 * waves * M * 32 * 4;
+}
 
 struct GemvPlan {
-  int kind;      // kGemvStream: persistent, whole K per workgroup, no workspace
+  int kind;      // kGemvStream: persistent VALU, whole K per workgroup, no workspace
+                 // kGemvMfma: the same with the dot on FP4 MFMA
                  // kGemvSplit: one workgroup per (tile, K slice), split-K tail
   int kc;        // K_pad / 64 chunks
   int tiles;     // N_pad / 32 row tiles

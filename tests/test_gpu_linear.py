@@ -62,10 +62,22 @@ UNIT_SHAPES = [(256, 512), (4096, 4096), (24576, 4096), (4096, 12288), (5120, 81
                (100, 1040), (33, 16), (64, 25600)]
 
 
+KERNELS = {"auto": 0, "valu_stream": 1, "split": 2, "mfma": 3}
+
+
+@pytest.fixture
+def kernel(nv, request):
+    """Force one GEMV kernel for the test (0 = the library's own choice)."""
+    nv.set_option("kernel", KERNELS[request.param])
+    yield request.param
+    nv.set_option("kernel", 0)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
 @pytest.mark.parametrize("N,K", UNIT_SHAPES)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
-def test_unit_scale_bit_exact(nv, M, N, K):
-    note(f"linear unit-scale M={M} N={N} K={K}")
+def test_unit_scale_bit_exact(nv, kernel, M, N, K):
+    note(f"linear unit-scale kernel={kernel} M={M} N={N} K={K}")
     xq, wq, ox, ow = _unit_operands(nv, M, N, K, seed=M * 7 + N % 13)
     y = nv.linear(xq, wq)
     _sync()
@@ -77,12 +89,13 @@ def test_unit_scale_bit_exact(nv, M, N, K):
                              f"{got[bad[0][0], bad[1][0]]} vs {ref[bad[0][0], bad[1][0]]}"
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
-def test_power_of_two_scales_bit_exact(nv, M):
+@pytest.mark.parametrize("kernel", ["auto", "valu_stream", "split", "mfma"], indirect=True)
+@pytest.mark.parametrize("M", [1, 3, 4, 8])
+def test_power_of_two_scales_bit_exact(nv, kernel, M):
     """Block scales 2^-2 .. 2^2 keep every partial sum a small dyadic
     rational, still exact in binary32."""
     N, K = 512, 2048
-    note(f"linear pow2-scale M={M} N={N} K={K}")
+    note(f"linear pow2-scale kernel={kernel} M={M} N={N} K={K}")
     xq, wq, ox, ow = _unit_operands(nv, M, N, K, seed=11 + M,
                                     scale_bytes=[0x28, 0x30, 0x38, 0x40, 0x48])
     y = nv.linear(xq, wq)
@@ -141,22 +154,24 @@ def test_tiny_full(nv):
     _check_sampled(nv, y, w16, x16, wq, np.arange(L.N))
 
 
+@pytest.mark.parametrize("kernel", ["auto", "mfma"], indirect=True)
 @pytest.mark.parametrize("lin", range(4))
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
-def test_8b_shapes_sampled(nv, lin, M):
+def test_8b_shapes_sampled(nv, kernel, lin, M):
     L = QWEN3_8B[lin]
-    note(f"linear 8B {L.name} M={M} N={L.N} K={L.K}")
+    note(f"linear 8B {L.name} kernel={kernel} M={M} N={L.N} K={L.K}")
     w16, x16, wq, xq = _quantized_pair(nv, 3, lin, L, M, "outlier")
     y = nv.linear(xq, wq)
     _sync()
     _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(lin)))
 
 
+@pytest.mark.parametrize("kernel", ["auto", "mfma"], indirect=True)
 @pytest.mark.parametrize("lin", range(4))
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_32b_shapes_sampled(nv, lin, M):
+def test_32b_shapes_sampled(nv, kernel, lin, M):
     L = QWEN3_32B[lin]
-    note(f"linear 32B {L.name} M={M} N={L.N} K={L.K}")
+    note(f"linear 32B {L.name} kernel={kernel} M={M} N={L.N} K={L.K}")
     w16, x16, wq, xq = _quantized_pair(nv, 4, lin, L, M, "student_t")
     y = nv.linear(xq, wq)
     _sync()
@@ -174,10 +189,11 @@ def test_bf16_output(nv, M):
     _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(5)), out_bf16=True)
 
 
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
 @pytest.mark.parametrize("N,K,M", [(1, 16, 1), (33, 16, 8), (100, 1040, 3), (4097, 784, 5),
-                                   (31, 25600, 7)])
-def test_ragged_and_degenerate(nv, N, K, M):
-    note(f"linear ragged M={M} N={N} K={K}")
+                                   (31, 25600, 7), (300, 8000, 2)])
+def test_ragged_and_degenerate(nv, kernel, N, K, M):
+    note(f"linear ragged kernel={kernel} M={M} N={N} K={K}")
     w16 = weights_bf16(1, 7, N, K)
     x16 = activations_bf16(1, 7, M, K)
     wq = nv.quantize_weight(to_dev_bf16(w16))
@@ -198,9 +214,10 @@ def test_zero_activation_gives_zero(nv):
     assert torch.count_nonzero(y).item() == 0
 
 
-def test_run_to_run_bit_stable(nv):
-    L = QWEN3_8B[3]                      # down: split-K with several slices
-    note(f"linear determinism M=8 N={L.N} K={L.K}")
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
+def test_run_to_run_bit_stable(nv, kernel):
+    L = QWEN3_8B[3]
+    note(f"linear determinism kernel={kernel} M=8 N={L.N} K={L.K}")
     w16, x16, wq, xq = _quantized_pair(nv, 3, 3, L, 8, "outlier")
     ys = [nv.linear(xq, wq).cpu() for _ in range(5)]
     for y in ys[1:]:
@@ -210,7 +227,8 @@ def test_run_to_run_bit_stable(nv):
 KNOBS = [  # (kernel, split_k, chunks_per_wave, waves)
     (2, 1, 0, 0), (2, 2, 0, 0), (2, 3, 0, 0), (2, 7, 0, 0), (2, 0, 4, 0), (2, 0, 8, 0),
     (2, 0, 12, 0), (2, 0, 16, 0), (2, 0, 4, 8), (2, 0, 16, 8), (2, 0, 4, 16), (2, 0, 8, 16),
-    (2, 2, 0, 16), (1, 0, 0, 0), (1, 0, 0, 8), (1, 0, 0, 16),
+    (2, 2, 0, 16), (1, 0, 0, 0), (1, 0, 0, 8), (1, 0, 0, 16), (3, 0, 0, 0), (3, 0, 0, 4),
+    (3, 0, 0, 8),
 ]
 
 
