@@ -85,8 +85,10 @@ typedef enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 } nvfp4_out_dtype;
  * "nvfp4r.configure(gemv_max_m=2)" / "nvfp4r.status()" (section "Run
  * benchmarks", the Python wiring example). */
 typedef enum {
-  NVFP4_OPT_GEMV_MAX_M = 0,   /* M <= value uses the VALU GEMV; larger M uses
-                                 the FP4 MFMA GEMM.  0..8.                 */
+  NVFP4_OPT_GEMV_MAX_M = 0,   /* M <= value uses the VALU GEMV (M <= 3 only);
+                                 larger M the FP4 MFMA one.  0..8, default 0
+                                 (MFMA for every M, the faster one on
+                                 gfx950).                                   */
   NVFP4_OPT_SPLIT_K = 1,      /* 0 = heuristic; s >= 1 forces s K-slices.  */
   NVFP4_OPT_CHUNKS_PER_WAVE = 2, /* 0 = heuristic; else 64-element K chunks
                                  each wavefront streams per row tile (multiple
@@ -103,7 +105,16 @@ typedef enum {
                                  3 = persistent streaming GEMV with the dot
                                  on FP4 MFMA (falls back to split-K when the
                                  activation does not fit in LDS).          */
-  NVFP4_OPT_COUNT = 6
+  NVFP4_OPT_SPIN_LIMIT = 6,   /* 0 = default; else the number of polls the
+                                 activation quantizer makes for the other
+                                 workgroups' maxima before computing the
+                                 tensor amax on its own (same result; a low
+                                 value exercises that path).               */
+  NVFP4_OPT_GRID = 7,         /* 0 = heuristic (one streaming workgroup per
+                                 CU); else at most this many streaming
+                                 workgroups, 1..65536 (above 256 several may
+                                 share a CU).                               */
+  NVFP4_OPT_COUNT = 8
 } nvfp4_option;
 
 /* ABI version of this header (incremented on any signature change). */
@@ -144,16 +155,28 @@ nvfp4_status nvfp4_unpack_weight(const uint8_t* w_codes, const uint8_t* w_scales
                                  int64_t K, uint8_t* codes_rowmajor, uint8_t* scales_rowmajor,
                                  void* stream);
 
+/* Workspace bytes nvfp4_quantize_act needs: 0 when one workgroup covers the
+ * tensor (M * K <= 16384), else 16 (the record in which the workgroups
+ * combine their maxima).  0 also for arguments nvfp4_quantize_act rejects. */
+size_t nvfp4_act_workspace_bytes(int M, int64_t K);
+
 /* Activation quantization, every decode step (W4A4: the activations reach
  * the linear as NVFP4).  One tensor scale over the whole M x K input.
- *   x_bf16   [M][ldx] bf16, 1 <= M <= 8, ldx >= K, ldx % 8 == 0, 16-byte
- *            aligned base
+ *   x_bf16   [M][ldx] bf16, 1 <= M <= 8, M * K <= 2^22, ldx >= K,
+ *            ldx % 8 == 0, 16-byte aligned base
  *   x_codes  [M][K/2] canonical;  x_scales [M][K/16] canonical
  *   x_gscale one float, written on the device (never read back to the host)
- */
+ *   workspace nvfp4_act_workspace_bytes bytes, 16-byte aligned, zeroed once
+ *            by nvfp4_workspace_init; each call leaves it zero again, so it
+ *            may be the same memory as nvfp4_linear's workspace when the
+ *            calls are ordered on one stream, but two calls that can run
+ *            concurrently need distinct workspaces.
+ * The tensor maximum is combined across workgroups inside the one kernel
+ * (each polls for the others a bounded number of times and otherwise
+ * computes it alone, so the call always terminates with the same result). */
 nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
                                 uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
-                                void* stream);
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes nvfp4_linear needs for this shape under the current
  * options: 0 when K is not split, else a fixed 64 KiB region of split-K

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_WORKSPACE, ERR_HIP = range(6)
 OUT_F32, OUT_BF16 = 0, 1
 OPTIONS = {"gemv_max_m": 0, "split_k": 1, "chunks_per_wave": 2, "nontemporal": 3, "waves": 4,
-           "kernel": 5}
+           "kernel": 5, "spin_limit": 6, "grid": 7}
 TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
 
 if not os.path.exists(LIB_PATH):
@@ -50,7 +50,8 @@ _quantize_weight = _sig("nvfp4_quantize_weight", _c_int, _vp, _c_i64, _c_i64, _c
                         _vp, _vp)
 _unpack_weight = _sig("nvfp4_unpack_weight", _c_int, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp)
 _quantize_act = _sig("nvfp4_quantize_act", _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
-                     _vp)
+                     _vp, _c_size, _vp)
+_act_workspace_bytes = _sig("nvfp4_act_workspace_bytes", _c_size, _c_int, _c_i64)
 _linear_workspace_bytes = _sig("nvfp4_linear_workspace_bytes", _c_size, _c_int, _c_i64, _c_i64)
 _workspace_init = _sig("nvfp4_workspace_init", _c_int, _vp, _c_size, _vp)
 _linear = _sig("nvfp4_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -97,6 +98,10 @@ def weight_bytes(N: int, K: int):
 
 def linear_workspace_bytes(M: int, N: int, K: int) -> int:
     return _linear_workspace_bytes(M, N, K)
+
+
+def act_workspace_bytes(M: int, K: int) -> int:
+    return _act_workspace_bytes(M, K)
 
 
 # ------------------------------------------------------------- torch glue
@@ -172,16 +177,19 @@ def empty_act(M: int, K: int, device="cuda") -> QuantAct:
                     torch.empty(1, dtype=torch.float32, device=device), M, K)
 
 
-def quantize_act(x, out: QuantAct | None = None) -> QuantAct:
+def quantize_act(x, out: QuantAct | None = None, ws=None) -> QuantAct:
     """bf16 [M][K] (row stride >= K, multiple of 8) -> canonical NVFP4 with
-    one tensor scale computed on the device."""
+    one tensor scale computed on the device.  `ws` defaults to the device's
+    shared workspace (stream-ordered use only)."""
     torch = _torch()
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
     M, K = x.shape
     q = out if out is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(1, 1, 16, x.device)
     _check(_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q.codes), _ptr(q.scales),
-                         _ptr(q.gscale), _stream(x)), "nvfp4_quantize_act")
+                         _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(x)), "nvfp4_quantize_act")
     return q
 
 

@@ -22,7 +22,7 @@ constexpr int kLayoutVersion = 1;
 constexpr int kMaxM = 8;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{8}, {0}, {0}, {1}, {0}, {0}};
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}};
 thread_local int t_last_hip = 0;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -81,9 +81,31 @@ void finish_workspace(GemvPlan& p, int M) {
   p.ws_bytes = p.splits > 1 ? nvfp4::kCounterBytes + p.ws_partials : 0;
 }
 
-// Launch plan of the VALU GEMV for (M, N, K) under the current knobs.
+constexpr int kStreamGrid = 256;   // one streaming workgroup per CU
+
+// K slices per row tile for the streaming kernels: with fewer than 64 row
+// tiles, enough (tile, slice) items to occupy more of the 256 workgroups,
+// without slices shorter than 8 chunks (512 elements).
+int stream_splits(int tiles, int kc) {
+  auto eff = [&](int s) {
+    const int64_t items = (int64_t)tiles * s;
+    const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
+    return (double)items / (double)(rounds * kStreamGrid);
+  };
+  // The split-K tail costs several dependent device-memory round trips, more
+  // than the idle CUs cost unless very few row tiles exist.
+  if (tiles >= 64 || eff(1) >= 0.85) return 1;
+  int best = 1;
+  for (int s = 2; s <= 8; ++s) {
+    if ((kc + s - 1) / s < 8) break;
+    if (eff(s) > eff(best) + 0.02) best = s;
+  }
+  return best;
+}
+
+// Launch plan of the GEMV for (M, N, K) under the current knobs.
 GemvPlan make_plan(int M, int64_t N, int64_t K) {
-  GemvPlan p;
+  GemvPlan p = {};
   p.kc = (int)(round_up(K, nvfp4::kGroupK) / nvfp4::kChunkK);
   p.tiles = (int)(round_up(N, nvfp4::kTileN) / nvfp4::kTileN);
   p.nontemporal = g_opts[NVFP4_OPT_NONTEMPORAL].load() ? 1 : 0;
@@ -92,29 +114,40 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
   const int64_t force_split = g_opts[NVFP4_OPT_SPLIT_K].load();
   const int64_t force_waves = g_opts[NVFP4_OPT_WAVES].load();
 
-  // Streaming kernels: one workgroup per CU walks whole row tiles (all of
-  // K), so no split-K reduction is needed; they need the whole activation in
-  // LDS.  Waves per workgroup = ceil(kc / cpw) so that every wave has work.
-  // M <= GEMV_MAX_M runs the VALU dot (M <= 3 only), larger M the MFMA dot.
+  // Streaming kernels: one workgroup per CU walks (row tile, K slice) items;
+  // they need the whole activation in LDS.  M <= GEMV_MAX_M runs the VALU
+  // dot (M <= 3 only), larger M the MFMA dot.
   const int64_t gemv_max_m = g_opts[NVFP4_OPT_GEMV_MAX_M].load();
-  const bool auto_kind = force_kernel == 0 && force_split == 0 && force_cpw == 0;
+  const bool auto_kind = force_kernel == 0 && force_cpw == 0;
   const bool want_mfma = force_kernel == 3 || (auto_kind && (M > gemv_max_m || M > 3));
   const bool want_valu = !want_mfma && (force_kernel == 1 || auto_kind) && M <= 3;
   if (want_mfma || want_valu) {
-    const int max_waves = want_mfma ? (M <= 3 ? 16 : 8) : (M == 1 ? 16 : 8);  // as compiled
-    const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves) : max_waves;
-    const int cpw = (int)round_up((p.kc + want - 1) / want, 4);
-    const int waves = (p.kc + cpw - 1) / cpw;
-    if (waves <= max_waves &&
-        (int64_t)nvfp4::stream_lds_need(M, p.kc, waves, want_mfma) <= kLdsBudget) {
+    const int max_waves = want_mfma ? 8 : (M == 1 ? 16 : 8);  // as compiled
+    const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves)
+                                     : std::min(max_waves, 8);
+    const int s0 = force_split > 0 ? (int)force_split : stream_splits(p.tiles, p.kc);
+    const int kcs = (p.kc + s0 - 1) / s0;                 // chunks per slice
+    const int cpw = (int)round_up((kcs + want - 1) / want, 4);
+    const int waves = (kcs + cpw - 1) / cpw;
+    const int cps = cpw * waves;
+    const int splits = (p.kc + cps - 1) / cps;
+    const int64_t items = (int64_t)p.tiles * splits;
+    const int64_t force_grid = g_opts[NVFP4_OPT_GRID].load();
+    const int grid = (int)std::min<int64_t>(items, force_grid > 0 ? force_grid : kStreamGrid);
+    const int64_t per_wg = (items + grid - 1) / grid;
+    const int64_t act = (int64_t)nvfp4::stream_act_lds(M, p.kc, want_mfma);
+    const int64_t slot = (int64_t)waves * M * 32 * 4;
+    const int64_t batch = std::min<int64_t>(per_wg, (kLdsBudget - act) / slot);
+    if (waves <= max_waves && batch >= 1 &&
+        (splits == 1 || per_wg <= batch * waves * M * 32)) {
       p.kind = want_mfma ? nvfp4::kGemvMfma : nvfp4::kGemvStream;
       p.waves = waves;
       p.depth = 12;
       p.cpw = cpw;
-      p.cps = cpw * waves;
-      p.splits = 1;
-      // one resident workgroup per CU (the launch reserves enough LDS)
-      p.grid = std::min(p.tiles, 256);
+      p.cps = cps;
+      p.splits = splits;
+      p.batch = (int)batch;
+      p.grid = grid;        // <= 256: one resident workgroup per CU (the launch reserves LDS)
       finish_workspace(p, M);
       return p;
     }
@@ -191,6 +224,12 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
     case NVFP4_OPT_KERNEL:
       if (value < 0 || value > 3) return NVFP4_ERR_INVALID_ARG;
       break;
+    case NVFP4_OPT_SPIN_LIMIT:
+      if (value < 0 || value > (int64_t(1) << 30)) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_GRID:
+      if (value < 0 || value > 65536) return NVFP4_ERR_INVALID_ARG;
+      break;
     default: return NVFP4_ERR_UNSUPPORTED;
   }
   g_opts[opt].store(value);
@@ -238,18 +277,31 @@ nvfp4_status nvfp4_unpack_weight(const uint8_t* w_codes, const uint8_t* w_scales
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
+size_t nvfp4_act_workspace_bytes(int M, int64_t K) {
+  if (M < 1 || M > kMaxM || K < 16 || K % 16 != 0 || (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks)
+    return 0;
+  return nvfp4::act_plan(M, K).groups > 1 ? nvfp4::kActSyncBytes : 0;
+}
+
 nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
                                 uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
-                                void* stream) {
-  if (!x_bf16 || !x_codes || !x_scales || !x_gscale) return NVFP4_ERR_INVALID_ARG;
-  if (M < 1 || K < 16 || K % 16 != 0 || K > (int64_t(1) << 28) || ldx < K || ldx % 8 != 0)
-    return M > kMaxM ? NVFP4_ERR_UNSUPPORTED : NVFP4_ERR_INVALID_ARG;
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (!x_bf16 || !x_codes || !x_scales || !x_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || K < 16 || K % 16 != 0 || (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks ||
+      ldx < K || ldx % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4))
     return NVFP4_ERR_INVALID_ARG;
+  const size_t need = nvfp4_act_workspace_bytes(M, K);
+  if (need > 0) {
+    if (!workspace || !aligned(workspace, 16)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  }
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
-  const hipError_t e = nvfp4::launch_quantize_act(x_bf16, M, (int)K, ldx, x_codes, x_scales,
-                                                  x_gscale, (hipStream_t)stream);
+  const hipError_t e = nvfp4::launch_quantize_act(
+      x_bf16, M, (int)K, ldx, x_codes, x_scales, x_gscale, static_cast<uint32_t*>(workspace),
+      (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(), (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
@@ -291,7 +343,7 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
   const hipError_t e =
       p.kind != nvfp4::kGemvSplit
           ? nvfp4::launch_gemv_stream(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,
-                                      w_gscale, y, out_dtype, (hipStream_t)stream)
+                                      w_gscale, y, out_dtype, workspace, (hipStream_t)stream)
           : nvfp4::launch_gemv_split(p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales,
                                      w_gscale, y, out_dtype, workspace, (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);

@@ -36,6 +36,8 @@ struct GemvArgs {
   int out_bf16;
   int nontemporal;
   int tiles;
+  int batch;     // streaming kernels: items reduced together (LDS slots)
+  int waves;     // streaming kernels: wavefronts per workgroup
 };
 
 __device__ inline u32x4 load_codes(const uint8_t* p, bool nt) {

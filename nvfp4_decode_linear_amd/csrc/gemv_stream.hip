@@ -1,25 +1,28 @@
-// Persistent streaming VALU GEMV for the small-M NVFP4 W4A4 decode linear
-// (gfx950): the default kernel whenever the whole K extent of the decoded
+// Persistent streaming GEMV for the small-M NVFP4 W4A4 decode linear
+// (gfx950): the default kernels whenever the whole K extent of the
 // activation fits in LDS.
 //
 // The operation is the one of "ReSET" GitHub README, "Core components",
-// item 2 (nvfp4r): for M <= 8 rows the FP4 weights are streamed once through
-// the vector ALUs and every loaded weight serves all M rows.  On gfx950:
+// item 2 (nvfp4r): for M <= 8 rows the FP4 weights are streamed once and
+// every loaded weight serves all M rows.  On gfx950:
 //
-//  * one workgroup of up to 16 wavefronts per CU walks row tiles blockIdx.x,
-//    blockIdx.x + gridDim.x, ...; inside a tile wave w owns the K chunks
-//    [w * cpw, (w + 1) * cpw), so a tile needs no reduction outside the
-//    workgroup and the kernel needs no workspace;
-//  * every wave keeps 3 or 4 groups of 4 weight records (1 KiB each, one
-//    64-lane load) in flight and refills a group as soon as it has consumed
-//    it; the wave's records of consecutive tiles form one stream, so the
-//    loads of the next tile are already in flight while this tile finishes;
-//  * the activation is decoded once per workgroup, for the whole K, into LDS
-//    as f16 x~ = e2m1(code) * e4m3(scale) (exact); the decode overlaps the
-//    first ring loads because its global loads are issued first;
-//  * a tile's partial sums meet in LDS (fixed wave order, so the result is
-//    the same on every run), are scaled by both tensor scales and written as
-//    binary32 or bf16.
+//  * one workgroup of up to 16 wavefronts per CU walks work items blockIdx.x,
+//    blockIdx.x + gridDim.x, ...; an item is a 32-row tile and a K slice
+//    (normally all of K), whose 4-record groups go to the waves round robin;
+//  * every wave keeps 3 groups of 4 weight records (1 KiB each, one 64-lane
+//    load) plus their scale record in flight and refills a group as soon as
+//    it has consumed it; the wave's groups of consecutive items form one
+//    stream, so the next item's loads are in flight while this one finishes;
+//  * the dot: either on FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+//    E8M0 scales on a block-diagonal activation operand, giving exact
+//    per-16-block partial dot products that the VALU scales by both E4M3
+//    block scales), or on the VALU (the activation decoded once into LDS as
+//    f16 x~ = e2m1(code) * e4m3(scale), exact, then v_dot2 per block);
+//  * an item's partial sums are left per wave in LDS and summed in fixed
+//    wave order (the same result on every run) once per batch of items, then
+//    scaled by both tensor scales and written as binary32 or bf16; with
+//    several K slices they go through the workspace instead, and the last
+//    slice of a tile to arrive sums the slices in slice order.
 #include <type_traits>
 
 #include "gemv_common.hpp"
@@ -30,7 +33,8 @@ namespace {
 
 using namespace gemv;
 
-constexpr int kStreamXpt = 4;   // activation blocks per thread issued ahead of the ring
+constexpr int kStreamXpt = 4;   // activation blocks per thread in the first batch
+constexpr int kStreamXrest = 8; // ... and in each later batch (large M * K)
 
 // Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
 // activation row, 8 (<= 256 VGPRs) for two or three rows, whose register
@@ -42,9 +46,12 @@ constexpr int stream_max_waves(int M) { return M == 1 ? 16 : 8; }
 // Groups of 4 weight records (4 KiB) each wave keeps in flight.
 constexpr int stream_ring_groups(int M) { return M == 3 ? 2 : 3; }
 
-// The MFMA variant keeps 16 result registers per chunk but decodes nothing.
-constexpr int mfma_max_waves(int M) { return M <= 3 ? 16 : 8; }
-constexpr int mfma_ring_groups(int) { return 3; }
+// The MFMA variant keeps 16 result registers per chunk but decodes nothing;
+// its ring has a spare slot (3 groups in flight while it computes, 4 for
+// four or more rows, whose longer epilogue needs the longer lookahead), which
+// needs the 256-register budget of 8 waves.
+constexpr int mfma_max_waves(int) { return 8; }
+constexpr int mfma_ring_groups(int M) { return M >= 4 ? 4 : 3; }
 
 // The grid holds at most one workgroup per CU.  The hardware dispatcher
 // packs workgroups onto a CU while its registers and LDS last, so every
@@ -55,14 +62,74 @@ constexpr size_t kStreamLdsReserve = 80 * 1024 + 1024;
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// f(ic<0>), f(ic<1>), ..., f(ic<N - 1>), unrolled at compile time
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (I < N) {
+      f(ic<I>{});
+      StaticFor<I + 1, N>::run(f);
+    }
+  }
+};
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  StaticFor<0, N>::run(f);
+}
+
+// Split-K tail of the streaming kernels, after the workgroup's last item:
+// wait until its partial sums are stored, count each of its items in at its
+// row tile's arrival counter (thread j takes item j, so the atomics overlap),
+// and for every tile where this workgroup arrived last, sum the slices in
+// slice order (the result does not depend on arrival order), scale, store,
+// and put the counter back to zero for the next call.  At most batch * NW *
+// M * 32 items per workgroup (the flags reuse the reduction slots).
+template <int M>
+__device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g, float* red) {
+  const int S = a.splits, G = gridDim.x;
+  uint32_t* flag = reinterpret_cast<uint32_t*>(red);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int nt = 64 * a.waves;
+  for (int j = threadIdx.x; j < nitem; j += nt) {
+    const int tile = ((int)blockIdx.x + j * G) / S;
+    const uint32_t old =
+        __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[j] = old == (uint32_t)(S - 1);
+  }
+  __syncthreads();
+  // every (item, row, column) of the items this workgroup completes at once
+  for (int i = threadIdx.x; i < nitem * M * 32; i += nt) {
+    const int j = i / (M * 32), mn = i - j * (M * 32);
+    if (!flag[j]) continue;
+    const int m = mn >> 5, n = mn & 31;
+    const int n0 = ((int)blockIdx.x + j * G) / S * kTileN;
+    const float* pp = a.part + (int64_t)m * a.n_pad + n0 + n;
+    const int64_t st = (int64_t)M * a.n_pad;
+    float v = 0.0f;
+    for (int t = 0; t < S; ++t)
+      v += __hip_atomic_load(pp + t * st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n0 + n < a.N) store_y(a, m, n0 + n, v * g);
+  }
+  for (int j = threadIdx.x; j < nitem; j += nt) {
+    if (flag[j]) {
+      const int tile = ((int)blockIdx.x + j * G) / S;
+      __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // One workgroup's whole job.  Every wave keeps RG groups of 4 weight records
 // in flight.  The numbers of groups the stream starts with and ends with are
 // compile-time constants on every path (the paths never merge), so the
 // compiler's memory wait counts stay exact: where paths with different
 // numbers of outstanding loads merge, it waits for all of them.
-template <int M, int RG, bool MF>
+template <int M, int RG, int XS, bool MF, bool SPLIT>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
-  const int NW = blockDim.x >> 6;
+  const int NW = a.waves;                     // = blockDim.x / 64 (not read from the
+                                              // dispatch packet: that load would
+                                              // delay every other one)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
@@ -70,72 +137,94 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const int kc = a.kc;
   const int row_dw = kc * 32;
   // VALU: x~ as f16 pairs [M][kc * 32 dwords].  MFMA: raw activation codes
-  // [M][kc * 4 blocks][2 dwords], then the E4M3 activation scales as floats
-  // [kc * 4 blocks][M].  Either is followed by the reduction array
-  // [2][NW][M][32] floats.
+  // [M][kc * 4 blocks][2 dwords], then the E4M3 activation scales as f16
+  // (every E4M3 value is an f16 value) [kc * 4 blocks][M], padded to a
+  // dword.  Either is followed by the reduction slots [batch][NW][M][32]
+  // floats.
   uint32_t* xlds = lds;
-  float* sa = reinterpret_cast<float*>(lds + M * kc * 8);
-  float* red = reinterpret_cast<float*>(MF ? lds + M * kc * 8 + kc * 4 * M : lds + M * row_dw);
+  _Float16* sa = reinterpret_cast<_Float16*>(lds + M * kc * 8);
+  float* red = reinterpret_cast<float*>(MF ? lds + M * kc * 8 + (kc * 4 * M + 1) / 2
+                                           : lds + M * row_dw);
   const int kb_row = a.K >> 4;
   const int nblk = M * kc * 4;                // activation 16-blocks, padded K
-  const int cpw = a.cpw;                      // chunks per wave per tile, multiple of 4
-  const int wc0 = wave * cpw;
-  const int wlast = min(wc0 + cpw, kc) - 1;   // last real chunk of this wave
+  const int cpw = a.cpw;                      // chunks per wave per item, multiple of 4
+
+  const int S = SPLIT ? a.splits : 1;         // K slices per row tile
   const int G = gridDim.x;
-  const int ntile = (a.tiles - (int)blockIdx.x + G - 1) / G;
-  const int ng = ntile * (cpw >> 2);          // groups of 4 records in this wave's stream
-
-  // ---- 1. activation blocks, first batch (issued before any weight load;
-  // out-of-range blocks read block 0 and are zeroed, so no load is
-  // conditional and the decode below waits only for these loads)
-  u32x2 xc[kStreamXpt];
-  uint32_t xs[kStreamXpt];
-#pragma unroll
-  for (int r = 0; r < kStreamXpt; ++r) {
-    const int i = threadIdx.x + r * 64 * NW;
-    const int m = i / (kc * 4), kb = i - m * (kc * 4);
-    const bool ok = i < nblk && kb < kb_row;
-    const int64_t cofs = ok ? (int64_t)m * (a.K >> 1) + 8 * kb : 0;
-    const int64_t sofs = ok ? (int64_t)m * kb_row + kb : 0;
-    xc[r] = *reinterpret_cast<const u32x2*>(a.xc + cofs);
-    xs[r] = a.xs[sofs];
-    if (!ok) {
-      xc[r] = u32x2{0u, 0u};
-      xs[r] = 0u;
+  const int nitem = (a.tiles * S - (int)blockIdx.x + G - 1) / G;
+  const int ng = nitem * (cpw >> 2);          // groups of 4 records in this wave's stream
+  // Work item i = (row tile i / S, K slice i % S).  The slice's chunks go
+  // to the waves in groups of 4 (one scale record), round robin: this wave
+  // owns chunks cb + NW * 4j + k (j < cpw / 4, k < 4, cb = slice * cps + 4 *
+  // wave), so at any time the workgroup's waves read adjacent records.  A
+  // group past K (last slice only) re-reads the tile's last group, with its
+  // scales zeroed.
+  struct Item {
+    int tile, slice, cb;
+  };
+  auto item = [&](int i) __attribute__((always_inline)) {
+    Item it;
+    if constexpr (SPLIT) {
+      it.tile = i / S;
+      it.slice = i - it.tile * S;
+    } else {
+      it.tile = i;
+      it.slice = 0;
     }
-  }
+    it.cb = it.slice * a.cps + 4 * wave;
+    return it;
+  };
 
-  // ---- 2. this wave's records form one stream: its cpw chunks of the
-  // workgroup's first tile, then of its second tile, ...  Chunks past K
-  // (only in the last wave) re-read the wave's last real chunk.
+  // ---- 1. this wave's records form one stream: its cpw chunks of the
+  // workgroup's first item, then of its second item, ...
   const uint8_t* wbase = a.wc + 16 * lane;
   const uint8_t* sbase = a.ws + 8 * lane;
-  int lt = blockIdx.x, loff = 0;              // load cursor: tile, chunk offset
-  u32x4 ring[RG][4];
-  u32x2 rsc[RG];
+  int li = blockIdx.x, loff = 0;              // load cursor: item, chunk offset
+  Item lit = item(li);
+  u32x4 ring[RG + XS][4];
+  u32x2 rsc[RG + XS];
   auto refill = [&](auto Q) __attribute__((always_inline)) {
     constexpr int q = decltype(Q)::value;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int64_t r = (int64_t)lt * kc + min(wc0 + loff + k, wlast);
+      const int64_t r = (int64_t)lit.tile * kc + min(lit.cb + loff * NW + k, kc - 4 + k);
       if (k == 0) rsc[q] = load_scales(sbase + (r >> 2) * kScaleRecord, nt);
       ring[q][k] = load_codes(wbase + r * kCodeRecord, nt);
     }
     loff += 4;
     if (loff == cpw) {
       loff = 0;
-      lt += G;
+      li += G;
+      lit = item(li);
     }
   };
 
-  // ---- 3. activation into LDS: the first batch from registers, any rest
-  // (large M * K only) read now.
+  // ---- 2. activation into LDS, after the first weight loads are issued
+  // (so no weight load waits behind it): a first batch of blocks per thread
+  // loaded together (out-of-range blocks read block 0 and are zeroed, so no
+  // load is conditional), any rest (large M * K only) after it.
   auto prologue = [&]() __attribute__((always_inline)) {
+    u32x2 xc[kStreamXpt];
+    uint32_t xs[kStreamXpt];
+#pragma unroll
+    for (int r = 0; r < kStreamXpt; ++r) {
+      const int i = threadIdx.x + r * 64 * NW;
+      const int m = i / (kc * 4), kb = i - m * (kc * 4);
+      const bool ok = i < nblk && kb < kb_row;
+      const int64_t cofs = ok ? (int64_t)m * (a.K >> 1) + 8 * kb : 0;
+      const int64_t sofs = ok ? (int64_t)m * kb_row + kb : 0;
+      xc[r] = *reinterpret_cast<const u32x2*>(a.xc + cofs);
+      xs[r] = a.xs[sofs];
+      if (!ok) {
+        xc[r] = u32x2{0u, 0u};
+        xs[r] = 0u;
+      }
+    }
     auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
       if constexpr (MF) {
         xlds[(m * kc * 4 + kb) * 2] = c.x;
         xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
-        sa[kb * M + m] = e4m3_to_f32(sc);
+        sa[kb * M + m] = (_Float16)e4m3_to_f32(sc);
       } else {
         decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
       }
@@ -148,15 +237,29 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         put(m, kb, xc[r], xs[r]);
       }
     }
-    for (int i = threadIdx.x + kStreamXpt * 64 * NW; i < nblk; i += 64 * NW) {
-      const int m = i / (kc * 4), kb = i - m * (kc * 4);
-      u32x2 c = {0u, 0u};
-      uint32_t sc = 0u;
-      if (kb < kb_row) {
-        c = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
-        sc = a.xs[(int64_t)m * kb_row + kb];
+    // the rest in batches of kStreamXrest blocks per thread, all loads of a
+    // batch in flight together
+    for (int base = threadIdx.x + kStreamXpt * 64 * NW; base < nblk;
+         base += kStreamXrest * 64 * NW) {
+      u32x2 c[kStreamXrest];
+      uint32_t sc[kStreamXrest];
+#pragma unroll
+      for (int r = 0; r < kStreamXrest; ++r) {
+        const int i = min(base + r * 64 * NW, nblk - 1);
+        const int m = i / (kc * 4), kb = i - m * (kc * 4);
+        const int kbc = min(kb, kb_row - 1);
+        c[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kbc);
+        sc[r] = a.xs[(int64_t)m * kb_row + kbc];
       }
-      put(m, kb, c, sc);
+#pragma unroll
+      for (int r = 0; r < kStreamXrest; ++r) {
+        const int i = base + r * 64 * NW;
+        if (i < nblk) {
+          const int m = i / (kc * 4), kb = i - m * (kc * 4);
+          const bool ok = kb < kb_row;
+          put(m, kb, ok ? c[r] : u32x2{0u, 0u}, ok ? sc[r] : 0u);
+        }
+      }
     }
     __syncthreads();
   };
@@ -166,32 +269,56 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  // Tile-boundary reduction: K halves (lanes l, l ^ 32), then waves in fixed
-  // order through a double-buffered LDS array (so one barrier per tile).
-  int ct = blockIdx.x, buf = 0;
+  // Item-boundary reduction.  The K halves meet at once (lanes l, l ^ 32);
+  // each wave then leaves its partial sum of the item in its own LDS slot
+  // [item in batch][wave][M][32] and streams on without waiting for the
+  // other waves.  After `batch` items (normally all of the workgroup's), one
+  // barrier, then the waves' partials are summed in fixed wave order (the
+  // result is the same on every run) and stored: as the output with one K
+  // slice, else as the slice's partial sum (device-coherent, combined after
+  // the stream), then a barrier before the slots are reused.
+  int ci = blockIdx.x, jb = 0, done = 0, batch_first = blockIdx.x;
+  Item cit = item(ci);
+  auto flush = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < jb * M * 32; i += 64 * NW) {
+      const int j = i / (M * 32), mn = i - j * (M * 32);
+      const float* sl = red + j * (NW * M * 32) + mn;
+      float v = sl[0];
+      for (int q = 1; q < NW; ++q) v += sl[q * M * 32];
+      const Item it = item(batch_first + j * G);
+      const int m = mn >> 5, n = it.tile * kTileN + (mn & 31);
+      if constexpr (SPLIT) {
+        __hip_atomic_store(a.part + ((int64_t)it.slice * M + m) * a.n_pad + n, v,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (n < a.N) store_y(a, m, n, v * g);
+      }
+    }
+    __syncthreads();
+    jb = 0;
+  };
   auto finish_tile = [&]() __attribute__((always_inline)) {
-    float* rb = red + buf * (NW * M * 32);
+    float* sl = red + jb * (NW * M * 32) + wave * (M * 32);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       acc[m] += __shfl_xor(acc[m], 32, 64);
-      if (h == 0) rb[(wave * M + m) * 32 + lane] = acc[m];
+      if (h == 0) sl[m * 32 + lane] = acc[m];
       acc[m] = 0.0f;
     }
-    __syncthreads();
-    const int n0 = ct * kTileN;
-    for (int i = threadIdx.x; i < M * 32; i += 64 * NW) {
-      const int m = i >> 5, n = i & 31;
-      float v = rb[m * 32 + n];
-      for (int q = 1; q < NW; ++q) v += rb[(q * M + m) * 32 + n];
-      if (n0 + n < a.N) store_y(a, m, n0 + n, v * g);
+    ++jb;
+    ++done;
+    ci += G;
+    cit = item(ci);
+    if (jb == a.batch || done == nitem) {
+      flush();
+      batch_first = ci;
     }
-    buf ^= 1;
-    ct += G;
   };
 
-  // Consume ring group q: chunks coff .. coff + 3 of the current tile.  Branch
-  // free (wait counts stay exact): a chunk past K (last wave only) reads a
-  // valid activation chunk and gets a zero block scale, so it adds exactly 0.
+  // Consume ring group q: chunks cb + NW * coff + 0..3 of the current item.
+  // Branch free (wait counts stay exact): a chunk past K reads a valid
+  // activation chunk and gets a zero block scale, so it adds exactly 0.
   // MFMA A operand: lane l holds row r = l % 32 of the 32 x 64 block-diagonal
   // activation tile, K half l / 32.  Row r is activation row ma, block ja of
   // the chunk, chosen so that the 32 x 32 result lands with every lane
@@ -212,7 +339,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     constexpr int q = decltype(Q)::value;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int c = wc0 + coff + k;
+      const int c = cit.cb + coff * NW + k;
       uint32_t sb = (k < 2 ? rsc[q].x : rsc[q].y) >> (16 * (k & 1));
       sb = c < kc ? sb : 0u;
       const int cx = min(c, kc - 1);
@@ -227,12 +354,12 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
                                                                        0, 127);
         const float sw0 = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
         const float sw1 = __builtin_amdgcn_cvt_f32_fp8(sb, 1);
-        const float* sap = sa + (4 * cx + 2 * h) * M;          // [block 2h + b][m]
+        const _Float16* sap = sa + (4 * cx + 2 * h) * M;       // [block 2h + b][m]
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = 2 * (v >> 2) + ((v & 3) >> 1), b = v & 1;
           if constexpr (true) {
-            if (m < M) acc[m] = fmaf(C[v], sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
+            if (m < M) acc[m] = fmaf(C[v], (float)sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
           }
         }
       } else {
@@ -246,105 +373,104 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
   };
 
-  // Short stream (ng < RG groups): load it all, then consume it.
+  // The stream.  Group g of the wave's stream lives in slot g % SL; A = RG
+  // groups are loaded ahead.  With a spare slot (SL = A + 1) each step first
+  // issues the load of the group A ahead into the slot consumed by the
+  // previous step, then consumes its own group, so A groups stay in flight
+  // while the wave computes; without one (SL = A) it consumes, then reuses
+  // the slot.  The numbers of groups loaded and consumed on every path are
+  // compile-time constants, so the memory wait counts stay exact.
+  constexpr int A = RG, SL = RG + XS;
+  auto step = [&](auto T) __attribute__((always_inline)) {    // position t of SL
+    constexpr int t = decltype(T)::value;
+    if constexpr (SL > A) {
+      refill(ic<(t + A) % SL>{});
+      consume(ic<t % SL>{});
+    } else {
+      consume(ic<t % SL>{});
+      refill(ic<t % SL>{});
+    }
+  };
+  // last A + x groups, x of them still to load
+  auto tail = [&](auto X) __attribute__((always_inline)) {
+    constexpr int x = decltype(X)::value;
+    static_for<A + x>([&](auto T) __attribute__((always_inline)) {
+      constexpr int t = decltype(T)::value;
+      if constexpr (t < x) step(ic<t>{}); else consume(ic<t % SL>{});
+    });
+  };
+  // fewer than A groups in all: load them, then consume them
   auto short_stream = [&](auto NG) __attribute__((always_inline)) {
     constexpr int n = decltype(NG)::value;
-    static_assert(n >= 1 && n < RG, "a short stream fits the ring");
-    refill(ic<0>{});
-    if constexpr (n >= 2) refill(ic<(n >= 2 ? 1 : 0)>{});
-    if constexpr (n >= 3) refill(ic<(n >= 3 ? 2 : 0)>{});
+    static_for<n>([&](auto T) __attribute__((always_inline)) { refill(T); });
     prologue();
-    consume(ic<0>{});
-    if constexpr (n >= 2) consume(ic<(n >= 2 ? 1 : 0)>{});
-    if constexpr (n >= 3) consume(ic<(n >= 3 ? 2 : 0)>{});
+    static_for<n>([&](auto T) __attribute__((always_inline)) { consume(T); });
   };
 
-  // Long stream: prime RG groups, then consume a group and refill its slot
-  // with the group RG ahead; the tail consumes R = RG + r remaining groups,
-  // refilling only the first r slots.
-  auto step = [&](auto Q) __attribute__((always_inline)) {
-    consume(Q);
-    refill(Q);
-  };
-  // slot index clamped into the ring for code that is discarded when RG is small
-  auto slot = [](auto Q) { return ic<(decltype(Q)::value < RG ? decltype(Q)::value : 0)>{}; };
-  auto tail = [&](auto R) __attribute__((always_inline)) {
-    constexpr int r = decltype(R)::value;
-    static_assert(r < RG, "at most RG - 1 groups left to load");
-    if constexpr (r > 0) step(ic<0>{}); else consume(ic<0>{});
-    if constexpr (r > 1) step(slot(ic<1>{})); else consume(ic<1>{});
-    if constexpr (RG > 2) { if constexpr (r > 2) step(slot(ic<2>{})); else consume(slot(ic<2>{})); }
-    if constexpr (RG > 3) { if constexpr (r > 3) step(slot(ic<3>{})); else consume(slot(ic<3>{})); }
-    if constexpr (r > 0) consume(ic<0>{});
-    if constexpr (r > 1) consume(slot(ic<1>{}));
-    if constexpr (r > 2) consume(slot(ic<2>{}));
-  };
-
-  static_assert(RG >= 2 && RG <= 4, "ring of 2 to 4 groups");
-  if (ng >= RG) {
-    refill(ic<0>{});
-    refill(ic<1>{});
-    if constexpr (RG > 2) refill(ic<2>{});
-    if constexpr (RG > 3) refill(ic<3>{});
+  static_assert(A >= 2 && A <= 4 && SL <= 5, "ring of 2 to 5 slots");
+  if (ng >= A) {
+    static_for<A>([&](auto T) __attribute__((always_inline)) { refill(T); });
     prologue();
     int gi = 0;
-    for (; gi + 2 * RG <= ng; gi += RG) {
-      step(ic<0>{});
-      step(ic<1>{});
-      if constexpr (RG > 2) step(ic<2>{});
-      if constexpr (RG > 3) step(ic<3>{});
-    }
-    switch (ng - gi - RG) {                   // 0 .. RG - 1 groups still to load
+    for (; gi + SL + A <= ng; gi += SL) static_for<SL>(step);
+    switch (ng - gi - A) {                    // 0 .. SL - 1 groups still to load
       case 0: tail(ic<0>{}); break;
       case 1: tail(ic<1>{}); break;
-      case 2: if constexpr (RG > 2) tail(ic<(RG > 2 ? 2 : 0)>{}); break;
-      default: if constexpr (RG > 3) tail(ic<(RG > 3 ? 3 : 0)>{}); break;
+      case 2: if constexpr (SL > 2) tail(ic<(SL > 2 ? 2 : 0)>{}); break;
+      case 3: if constexpr (SL > 3) tail(ic<(SL > 3 ? 3 : 0)>{}); break;
+      default: if constexpr (SL > 4) tail(ic<(SL > 4 ? 4 : 0)>{}); break;
     }
   } else {
-    switch (ng) {                             // 1 .. RG - 1
+    switch (ng) {                             // 1 .. A - 1
       case 1: short_stream(ic<1>{}); break;
-      case 2: if constexpr (RG > 2) short_stream(ic<(RG > 2 ? 2 : 1)>{}); break;
-      default: if constexpr (RG > 3) short_stream(ic<(RG > 3 ? 3 : 1)>{}); break;
+      case 2: if constexpr (A > 2) short_stream(ic<(A > 2 ? 2 : 1)>{}); break;
+      default: if constexpr (A > 3) short_stream(ic<(A > 3 ? 3 : 1)>{}); break;
     }
   }
+  if constexpr (SPLIT) split_tail<M>(a, nitem, g, red);
 }
 
-// Launch: blockDim.x = 64 * NW (NW <= stream_max_waves(M), every wave owns at least one real
-// chunk of each tile); dynamic LDS = x~ [M][kc * 32] dwords followed by the
-// reduction array [2][NW][M][32] floats.
-template <int M>
+// Launch: blockDim.x = 64 * a.waves (at most stream_max_waves(M) or
+// mfma_max_waves(M)); dynamic LDS = the activation followed by the
+// reduction slots (stream_lds_need), at least kStreamLdsReserve.
+template <int M, bool SPLIT>
 __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, stream_ring_groups(M), false>(a, lds);
+  stream_body<M, stream_ring_groups(M), 0, false, SPLIT>(a, lds);
 }
 
-template <int M>
+template <int M, bool SPLIT>
 __global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, mfma_ring_groups(M), true>(a, lds);
+  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT>(a, lds);
+}
+
+template <int M, bool MF, bool SPLIT>
+hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch);
+  const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
+  const void* fn;
+  if constexpr (MF)
+    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT>);
+  else
+    fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M, SPLIT>);
+  static hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  if constexpr (MF)
+    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT>), dim3((unsigned)p.grid), dim3(64 * p.waves),
+                       lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_stream_kernel<M, SPLIT>), dim3((unsigned)p.grid),
+                       dim3(64 * p.waves), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int M, bool MF>
 hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
     return hipErrorInvalidValue;
-  const size_t need = stream_lds_need(M, p.kc, p.waves, MF);
-  const size_t lds = need > kStreamLdsReserve ? need : kStreamLdsReserve;
-  const void* fn;
-  if constexpr (MF)
-    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M>);
-  else
-    fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M>);
-  static hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  if constexpr (MF)
-    hipLaunchKernelGGL((gemv_mfma_kernel<M>), dim3((unsigned)p.grid), dim3(64 * p.waves), lds, s,
-                       a);
-  else
-    hipLaunchKernelGGL((gemv_stream_kernel<M>), dim3((unsigned)p.grid), dim3(64 * p.waves), lds,
-                       s, a);
-  return hipGetLastError();
+  return p.splits > 1 ? launch_ms<M, MF, true>(p, a, s) : launch_ms<M, MF, false>(p, a, s);
 }
 
 }  // namespace
@@ -352,7 +478,7 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, const uint8_t* xc,
                               const uint8_t* xs, const float* xg, const uint8_t* wc,
                               const uint8_t* ws, const float* wg, void* y, int out_bf16,
-                              hipStream_t s) {
+                              void* workspace, hipStream_t s) {
   GemvArgs a = {};
   a.xc = xc;
   a.xs = xs;
@@ -367,7 +493,14 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
   a.kc = p.kc;
   a.kg = p.kc / 4;
   a.cpw = p.cpw;
-  a.splits = 1;
+  a.cps = p.cps;
+  a.splits = p.splits;
+  a.batch = p.batch;
+  a.waves = p.waves;
+  a.part = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                   kCounterBytes)
+                        : nullptr;
+  a.cnt = static_cast<uint32_t*>(workspace);
   a.out_bf16 = out_bf16;
   a.nontemporal = p.nontemporal;
   a.tiles = p.tiles;

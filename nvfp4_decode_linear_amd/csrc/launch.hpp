@@ -18,22 +18,27 @@ enum GemvKind { kGemvStream = 0, kGemvSplit = 1, kGemvMfma = 2 };
 
 // Dynamic LDS bytes of a streaming workgroup (VALU or MFMA variant) with
 // `waves` wavefronts, before the reservation that keeps one workgroup per CU.
-inline size_t stream_lds_need(int M, int kc, int waves, bool mfma) {
-  const size_t act = mfma ? (size_t)M * kc * 32 + (size_t)kc * 4 * M * 4   // codes + scales
-                          : (size_t)M * kc * 128;                          // f16 x~
-  return act + (size_t)2 * waves * M * 32 * 4;
+// LDS bytes of a streaming-kernel workgroup: the activation (MFMA: codes and
+// f16 scales; VALU: f16 x~) plus `batch` item slots of per-wave partial sums.
+inline size_t stream_act_lds(int M, int kc, bool mfma) {
+  return mfma ? (size_t)M * kc * 32 + ((size_t)kc * 4 * M + 1) / 2 * 4
+              : (size_t)M * kc * 128;
+}
+inline size_t stream_lds_need(int M, int kc, int waves, bool mfma, int batch) {
+  return stream_act_lds(M, kc, mfma) + (size_t)batch * waves * M * 32 * 4;
 }
 
 struct GemvPlan {
-  int kind;      // kGemvStream: persistent VALU, whole K per workgroup, no workspace
+  int kind;      // kGemvStream: persistent VALU over (tile, K slice) items
                  // kGemvMfma: the same with the dot on FP4 MFMA
                  // kGemvSplit: one workgroup per (tile, K slice), split-K tail
   int kc;        // K_pad / 64 chunks
   int tiles;     // N_pad / 32 row tiles
   int cpw;       // chunks per wavefront (per tile and slice; multiple of 4)
   int waves;     // wavefronts per workgroup
-  int cps;       // chunks per K slice (= cpw * waves; split kernel)
-  int splits;    // K slices (split kernel; 1 for the stream kernel)
+  int cps;       // chunks per K slice (= cpw * waves)
+  int splits;    // K slices per row tile (1 = no split-K tail, no workspace)
+  int batch;     // streaming kernels: items whose partial sums share one barrier
   int depth;     // weight records in flight per wavefront (stream kernel)
   int grid;      // workgroups launched
   int nontemporal;
@@ -43,8 +48,20 @@ struct GemvPlan {
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+// Activation quantizer launch: `groups` workgroups of 256 threads, each
+// thread owning `bpt` (1, 2 or 4) blocks of 16.  Largest tensor: 256 * 256 *
+// 4 blocks (kActMaxBlocks).
+struct ActPlan {
+  int groups;
+  int bpt;
+};
+constexpr int64_t kActMaxBlocks = 256 * 256 * 4;
+constexpr size_t kActSyncBytes = 16;
+ActPlan act_plan(int M, int64_t K);
+
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
-                               uint8_t* scales, float* gscale, hipStream_t s);
+                               uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
+                               hipStream_t s);
 
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                   uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s);
@@ -62,6 +79,6 @@ hipError_t launch_gemv_split(const GemvPlan& p, int M, int64_t N, int64_t K,
 hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               const uint8_t* xc, const uint8_t* xs, const float* xg,
                               const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,
-                              int out_bf16, hipStream_t s);
+                              int out_bf16, void* workspace, hipStream_t s);
 
 }  // namespace nvfp4

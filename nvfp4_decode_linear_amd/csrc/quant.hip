@@ -36,15 +36,23 @@ __device__ inline uint32_t absmax_bits(const uint32_t (&v)[8]) {
 
 // ------------------------------------------------------------ activations
 //
-// One workgroup quantizes the whole M x K activation.  The tensor amax is a
-// reduction over every element (bf16 magnitudes compared as integers, exact)
-// and must be known before any block can be scaled.  When the tensor has at
-// most 4 blocks of 16 per thread (BPT > 0) each thread keeps its blocks in
-// registers between the reduction and the quantization; otherwise (BPT == 0)
-// the second pass re-reads the blocks (an L2 hit).  The tensor scale never
-// leaves the device.
-constexpr int kActThreads = 1024;
-constexpr int kActBpt = 4;
+// The tensor amax is a reduction over every element of the M x K activation
+// (bf16 magnitudes compared as integers, exact) and must be known before any
+// block can be scaled.  Each thread owns BPT blocks of 16 (block b0, b0 +
+// stride, ...), loads them all up front (clamped addresses, so no load is
+// conditional and all are in flight together) and keeps them in registers
+// through the reduction.  With more than one workgroup the workgroup maxima
+// meet in a 16-byte sync record of the caller's workspace:
+//   word 0: running amax (atomic max), word 1: arrivals, word 2: departures.
+// Thread 0 of each workgroup adds its maximum, arrives, and polls the
+// arrivals until all workgroups have arrived; the last workgroup to depart
+// puts all three words back to zero, so the record is zero between calls
+// (graph replays included).  The poll is bounded: a workgroup that gives up
+// (the grid is not co-resident, or the spin limit is forced low) computes
+// the amax itself from the whole tensor, which gives the same value.
+constexpr int kActThreads = 256;
+constexpr int kActMaxGroups = 256;
+constexpr uint32_t kActDefaultSpin = 1u << 20;
 
 __device__ inline uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
@@ -53,6 +61,7 @@ __device__ inline uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
   uint32_t all = 0;
 #pragma unroll
   for (int w = 0; w < kActThreads / kWave; ++w) all = max(all, red[w]);
+  __syncthreads();                              // red is reused
   return all;
 }
 
@@ -65,51 +74,83 @@ __device__ inline void store_block(uint8_t* codes, uint8_t* scales, int K, int m
   scales[(int64_t)m * (K >> 4) + j] = (uint8_t)q.scale;
 }
 
+// amax of the whole tensor by one workgroup (the fallback path)
+__device__ uint32_t tensor_amax_bits(const uint16_t* x, int M, int K, int64_t ldx, uint32_t* red) {
+  const int nbr = K >> 4, nb = M * nbr;
+  uint32_t amax = 0;
+  for (int b = threadIdx.x; b < nb; b += kActThreads) {
+    const int m = b / nbr, j = b - m * nbr;
+    uint32_t v[8];
+    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
+    amax = max(amax, absmax_bits(v));
+  }
+  return block_reduce_max(amax, red);
+}
+
 template <int BPT>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ gscale) {
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, uint32_t* sync,
+    uint32_t spin_limit) {
   __shared__ uint32_t red[kActThreads / kWave];
+  __shared__ uint32_t shared_amax;
   const int nbr = K >> 4;
   const int nb = M * nbr;
+  const int stride = gridDim.x * kActThreads;
+  const int b0 = blockIdx.x * kActThreads + threadIdx.x;
+  uint32_t v[BPT][8];
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int b = min(b0 + r * stride, nb - 1);
+    const int m = b / nbr, j = b - m * nbr;
+    load_block_bf16(x + (int64_t)m * ldx + 16 * j, v[r]);
+  }
   uint32_t amax = 0;
-  if constexpr (BPT > 0) {
-    uint32_t v[BPT][8];
 #pragma unroll
-    for (int r = 0; r < BPT; ++r) {
-      const int b = threadIdx.x + r * kActThreads;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[r][i] = 0u;
-      if (b < nb) {
-        const int m = b / nbr, j = b - m * nbr;
-        load_block_bf16(x + (int64_t)m * ldx + 16 * j, v[r]);
+  for (int r = 0; r < BPT; ++r) amax = max(amax, absmax_bits(v[r]));
+  amax = block_reduce_max(amax, red);
+
+  if (gridDim.x > 1) {
+    if (threadIdx.x == 0) {
+      const uint32_t G = gridDim.x;
+      __hip_atomic_fetch_max(sync, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t all = 0xFFFFFFFFu;                 // "gave up"
+      for (uint32_t i = 0;; ++i) {
+        const uint32_t c = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (c >= G) {
+          __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          all = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        if (i + 1 >= spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
       }
-      amax = max(amax, absmax_bits(v[r]));
-    }
-    const float sg = tensor_scale(bf16_to_f32(block_reduce_max(amax, red)));
-    if (threadIdx.x == 0) *gscale = sg;
-#pragma unroll
-    for (int r = 0; r < BPT; ++r) {
-      const int b = threadIdx.x + r * kActThreads;
-      if (b < nb) {
-        const int m = b / nbr, j = b - m * nbr;
-        store_block(codes, scales, K, m, j, quantize_block_bf16(v[r], sg));
+      shared_amax = all;
+      // depart (the amax load above has returned: its value is in `all`)
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const uint32_t d = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      if (d == G - 1) {                           // every workgroup has read: reset
+        __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  } else {
-    for (int b = threadIdx.x; b < nb; b += kActThreads) {
+    __syncthreads();
+    amax = shared_amax;
+    if (amax == 0xFFFFFFFFu) amax = tensor_amax_bits(x, M, K, ldx, red);
+  }
+
+  const float sg = tensor_scale(bf16_to_f32(amax));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = sg;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int b = b0 + r * stride;
+    if (b < nb) {
       const int m = b / nbr, j = b - m * nbr;
-      uint32_t v[8];
-      load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
-      amax = max(amax, absmax_bits(v));
-    }
-    const float sg = tensor_scale(bf16_to_f32(block_reduce_max(amax, red)));
-    if (threadIdx.x == 0) *gscale = sg;
-    for (int b = threadIdx.x; b < nb; b += kActThreads) {
-      const int m = b / nbr, j = b - m * nbr;
-      uint32_t v[8];
-      load_block_bf16(x + (int64_t)m * ldx + 16 * j, v);
-      store_block(codes, scales, K, m, j, quantize_block_bf16(v, sg));
+      store_block(codes, scales, K, m, j, quantize_block_bf16(v[r], sg));
     }
   }
 }
@@ -212,14 +253,41 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t word
 
 }  // namespace
 
+ActPlan act_plan(int M, int64_t K) {
+  const int64_t nb = (int64_t)M * (K >> 4);
+  ActPlan p;
+  if (nb <= 4 * kActThreads) {                  // one workgroup, up to 4 blocks per thread
+    p.groups = 1;
+    p.bpt = (int)((nb + kActThreads - 1) / kActThreads);
+  } else {
+    p.groups = (int)std::min<int64_t>((nb + kActThreads - 1) / kActThreads, kActMaxGroups);
+    p.bpt = (int)((nb + (int64_t)p.groups * kActThreads - 1) / ((int64_t)p.groups * kActThreads));
+  }
+  if (p.bpt == 3) p.bpt = 4;
+  return p;
+}
+
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
-                               uint8_t* scales, float* gscale, hipStream_t s) {
-  if ((int64_t)M * (K >> 4) <= (int64_t)kActThreads * kActBpt)
-    hipLaunchKernelGGL(act_quant_kernel<kActBpt>, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx,
-                       codes, scales, gscale);
-  else
-    hipLaunchKernelGGL(act_quant_kernel<0>, dim3(1), dim3(kActThreads), 0, s, x, M, K, ldx, codes,
-                       scales, gscale);
+                               uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
+                               hipStream_t s) {
+  const ActPlan p = act_plan(M, K);
+  const uint32_t spin = spin_limit ? spin_limit : kActDefaultSpin;
+  switch (p.bpt) {
+    case 1:
+      hipLaunchKernelGGL(act_quant_kernel<1>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
+                         ldx, codes, scales, gscale, sync, spin);
+      break;
+    case 2:
+      hipLaunchKernelGGL(act_quant_kernel<2>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
+                         ldx, codes, scales, gscale, sync, spin);
+      break;
+    case 4:
+      hipLaunchKernelGGL(act_quant_kernel<4>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
+                         ldx, codes, scales, gscale, sync, spin);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@ def lib():
     i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     L.nvfp4_linear.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                vp, sz, vp]
-    L.nvfp4_quantize_act.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp]
+    L.nvfp4_quantize_act.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.nvfp4_act_workspace_bytes.argtypes = [ctypes.c_int, i64]
+    L.nvfp4_act_workspace_bytes.restype = sz
     L.nvfp4_quantize_weight.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
     L.nvfp4_unpack_weight.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nvfp4_weight_bytes.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
@@ -69,11 +71,15 @@ def test_weight_bytes(lib):
 
 def test_options_roundtrip_and_validation(lib):
     v = ctypes.c_int64()
-    assert lib.nvfp4_get_option(0, ctypes.byref(v)) == 0 and v.value == 8
+    assert lib.nvfp4_get_option(0, ctypes.byref(v)) == 0 and v.value == 0
     assert lib.nvfp4_set_option(0, 2) == 0
     assert lib.nvfp4_get_option(0, ctypes.byref(v)) == 0 and v.value == 2
-    assert lib.nvfp4_set_option(0, 8) == 0
+    assert lib.nvfp4_set_option(0, 0) == 0
     assert lib.nvfp4_set_option(0, 9) == 1
+    assert lib.nvfp4_set_option(6, -1) == 1         # spin limit
+    assert lib.nvfp4_set_option(6, 1) == 0
+    assert lib.nvfp4_get_option(6, ctypes.byref(v)) == 0 and v.value == 1
+    assert lib.nvfp4_set_option(6, 0) == 0
     assert lib.nvfp4_set_option(2, 6) == 1          # chunks per wave must be a multiple of 4
     assert lib.nvfp4_set_option(3, 2) == 1
     assert lib.nvfp4_set_option(99, 0) == 2
@@ -84,14 +90,19 @@ def test_workspace_bytes(lib):
     assert lib.nvfp4_linear_workspace_bytes(9, 4096, 4096) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 4096, 24) == 0
     # The streaming kernel (the default whenever the activation fits in LDS)
-    # needs no workspace.
+    # needs no workspace unless it splits K, which it does only for fewer
+    # than 64 row tiles: N = 1024 (32 tiles) and K = 4096 split into 8
+    # slices: counters plus [8][M][N] partial sums.
+    assert lib.nvfp4_linear_workspace_bytes(1, 24576, 4096) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 4096, 4096) == 0
-    assert lib.nvfp4_linear_workspace_bytes(8, 5120, 25600) > 0      # too big for LDS: split-K
-    # Forcing the split-K kernel on the 8B O projection needs one: 64 KiB of
-    # counters plus [splits][M][N] partial sums.
+    assert lib.nvfp4_linear_workspace_bytes(1, 1024, 4096) == 64 * 1024 + 8 * 1024 * 4
+    assert lib.nvfp4_linear_workspace_bytes(8, 5120, 25600) == 0     # codes + f16 scales fit
+    assert lib.nvfp4_linear_workspace_bytes(8, 5120, 40960) > 0      # too big for LDS: split-K
+    # Forcing the split-K kernel on the 8B down projection (128 tiles) needs
+    # one.
     assert lib.nvfp4_set_option(5, 2) == 0
     try:
-        n = lib.nvfp4_linear_workspace_bytes(1, 4096, 4096)
+        n = lib.nvfp4_linear_workspace_bytes(1, 4096, 12288)
         assert n > 64 * 1024 and (n - 64 * 1024) % (4096 * 4) == 0
     finally:
         assert lib.nvfp4_set_option(5, 0) == 0
@@ -123,25 +134,42 @@ def test_linear_argument_errors(lib, no_gpu):
     bad = list(ok)
     bad[7] = 5
     assert f(1, 256, 512, *bad) == 1                          # unknown output dtype
-    # (8, 5120, 25600): too large for the streaming kernel, so split-K with a
+    # (8, 5120, 40960): the activation does not fit in LDS, so split-K with a
     # workspace
     bad = list(ok)
     bad[8] = ctypes.c_void_p(0x1001)
-    assert f(8, 5120, 25600, *bad) == 1                       # misaligned workspace
+    assert f(8, 5120, 40960, *bad) == 1                       # misaligned workspace
     bad = list(ok)
     bad[9] = 16
-    assert f(8, 5120, 25600, *bad) == 4                       # workspace too small
+    assert f(8, 5120, 40960, *bad) == 4                       # workspace too small
     bad = list(ok)
     bad[3] = ctypes.c_void_p(0x1008)
     assert f(1, 256, 512, *bad) == 1                          # misaligned tiled codes
 
 
+def test_act_workspace_bytes(lib):
+    assert lib.nvfp4_act_workspace_bytes(1, 4096) == 0          # 256 blocks: one workgroup
+    assert lib.nvfp4_act_workspace_bytes(4, 4096) == 0          # 1024 blocks: one workgroup
+    assert lib.nvfp4_act_workspace_bytes(8, 4096) == 16
+    assert lib.nvfp4_act_workspace_bytes(8, 25600) == 16
+    assert lib.nvfp4_act_workspace_bytes(8, 524288) == 16       # the largest tensor
+    assert lib.nvfp4_act_workspace_bytes(8, 524304) == 0        # rejected: too large
+    assert lib.nvfp4_act_workspace_bytes(9, 4096) == 0
+    assert lib.nvfp4_act_workspace_bytes(1, 24) == 0
+
+
 def test_quantize_argument_errors(lib, no_gpu):
-    assert lib.nvfp4_quantize_act(FAKE, 9, 512, 512, FAKE, FAKE, FAKE, None) == 2
-    assert lib.nvfp4_quantize_act(FAKE, 1, 520, 520, FAKE, FAKE, FAKE, None) == 1
-    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 500, FAKE, FAKE, FAKE, None) == 1   # ldx < K
-    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 516, FAKE, FAKE, FAKE, None) == 1   # ldx % 8
-    assert lib.nvfp4_quantize_act(None, 1, 512, 512, FAKE, FAKE, FAKE, None) == 1
+    q = lib.nvfp4_quantize_act
+    ws = (FAKE, 64, None)
+    assert q(FAKE, 9, 512, 512, FAKE, FAKE, FAKE, *ws) == 2
+    assert q(FAKE, 1, 520, 520, FAKE, FAKE, FAKE, *ws) == 1
+    assert q(FAKE, 1, 512, 500, FAKE, FAKE, FAKE, *ws) == 1   # ldx < K
+    assert q(FAKE, 1, 512, 516, FAKE, FAKE, FAKE, *ws) == 1   # ldx % 8
+    assert q(None, 1, 512, 512, FAKE, FAKE, FAKE, *ws) == 1
+    assert q(FAKE, 8, 524304, 524304, FAKE, FAKE, FAKE, *ws) == 1   # M * K > 2^22
+    assert q(FAKE, 8, 25600, 25600, FAKE, FAKE, FAKE, None, 0, None) == 1     # needs a workspace
+    assert q(FAKE, 8, 25600, 25600, FAKE, FAKE, FAKE, FAKE, 8, None) == 4     # too small
+    assert q(FAKE, 8, 25600, 25600, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1008), 64, None) == 1
     assert lib.nvfp4_quantize_weight(FAKE, 256, 24, 24, FAKE, FAKE, FAKE, None) == 1
     assert lib.nvfp4_quantize_weight(FAKE, 256, 512, 256, FAKE, FAKE, FAKE, None) == 1
     assert lib.nvfp4_quantize_weight(ctypes.c_void_p(0x1002), 256, 512, 512, FAKE, FAKE, FAKE,
@@ -152,6 +180,6 @@ def test_quantize_argument_errors(lib, no_gpu):
 
 
 def test_no_device_is_reported(lib, no_gpu):
-    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 512, FAKE, FAKE, FAKE, None) == 3
+    assert lib.nvfp4_quantize_act(FAKE, 1, 512, 512, FAKE, FAKE, FAKE, None, 0, None) == 3
     assert lib.nvfp4_linear(1, 256, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
                             1 << 20, None) == 3

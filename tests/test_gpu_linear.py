@@ -62,18 +62,24 @@ UNIT_SHAPES = [(256, 512), (4096, 4096), (24576, 4096), (4096, 12288), (5120, 81
                (100, 1040), (33, 16), (64, 25600)]
 
 
-KERNELS = {"auto": 0, "valu_stream": 1, "split": 2, "mfma": 3}
+KERNELS = {  # name: (kernel option, split_k option)
+    "auto": (0, 0), "valu_stream": (1, 0), "split": (2, 0), "mfma": (3, 1), "mfma_split3": (3, 3),
+}
 
 
 @pytest.fixture
 def kernel(nv, request):
-    """Force one GEMV kernel for the test (0 = the library's own choice)."""
-    nv.set_option("kernel", KERNELS[request.param])
+    """Force one GEMV kernel (and K slice count) for the test; "auto" is the
+    library's own choice."""
+    k, sp = KERNELS[request.param]
+    nv.set_option("kernel", k)
+    nv.set_option("split_k", sp)
     yield request.param
     nv.set_option("kernel", 0)
+    nv.set_option("split_k", 0)
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
 @pytest.mark.parametrize("N,K", UNIT_SHAPES)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
 def test_unit_scale_bit_exact(nv, kernel, M, N, K):
@@ -189,7 +195,7 @@ def test_bf16_output(nv, M):
     _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(5)), out_bf16=True)
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
 @pytest.mark.parametrize("N,K,M", [(1, 16, 1), (33, 16, 8), (100, 1040, 3), (4097, 784, 5),
                                    (31, 25600, 7), (300, 8000, 2)])
 def test_ragged_and_degenerate(nv, kernel, N, K, M):
@@ -214,7 +220,7 @@ def test_zero_activation_gives_zero(nv):
     assert torch.count_nonzero(y).item() == 0
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
 def test_run_to_run_bit_stable(nv, kernel):
     L = QWEN3_8B[3]
     note(f"linear determinism kernel={kernel} M=8 N={L.N} K={L.K}")
@@ -227,8 +233,9 @@ def test_run_to_run_bit_stable(nv, kernel):
 KNOBS = [  # (kernel, split_k, chunks_per_wave, waves)
     (2, 1, 0, 0), (2, 2, 0, 0), (2, 3, 0, 0), (2, 7, 0, 0), (2, 0, 4, 0), (2, 0, 8, 0),
     (2, 0, 12, 0), (2, 0, 16, 0), (2, 0, 4, 8), (2, 0, 16, 8), (2, 0, 4, 16), (2, 0, 8, 16),
-    (2, 2, 0, 16), (1, 0, 0, 0), (1, 0, 0, 8), (1, 0, 0, 16), (3, 0, 0, 0), (3, 0, 0, 4),
-    (3, 0, 0, 8),
+    (2, 2, 0, 16), (1, 0, 0, 0), (1, 0, 0, 8), (1, 0, 0, 16), (1, 2, 0, 0), (1, 4, 0, 8),
+    (3, 0, 0, 0), (3, 0, 0, 4), (3, 0, 0, 8), (3, 1, 0, 16), (3, 2, 0, 0), (3, 3, 0, 8),
+    (3, 5, 0, 4), (3, 16, 0, 0),
 ]
 
 

@@ -141,6 +141,71 @@ def test_act_quant_edges(nv):
     del torch
 
 
+def _sync_words(ws):
+    return ws[:16].cpu().numpy().view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("M,K", [(8, 25600), (3, 8192), (8, 4096), (8, 524288)])
+def test_act_quant_multi_workgroup_and_forced_fallback(nv, M, K):
+    """Tensors of more than 1024 blocks are spread over several workgroups
+    that combine their maxima through the workspace; with the spin limit
+    forced to 1 most workgroups give up polling and compute the amax alone.
+    Both paths must give the oracle's bits, and leave the record zero."""
+    import torch
+    x = activations_bf16(4, 9, M, K, "student_t")
+    xd = to_dev_bf16(x)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    assert nv.act_workspace_bytes(M, K) == 16
+    for spin in (0, 1):
+        note(f"act quant multi-workgroup M={M} K={K} spin_limit={spin}")
+        nv.set_option("spin_limit", spin)
+        try:
+            q = nv.quantize_act(xd, ws=ws)
+            _sync()
+        finally:
+            nv.set_option("spin_limit", 0)
+        _assert_act_equal(q, bf16_to_f32(x))
+        assert _sync_words(ws) == [0, 0, 0, 0]
+
+
+def test_act_quant_record_reuse_and_graph_replay(nv):
+    """One workspace serves consecutive calls of different sizes, and a
+    captured quantization replays correctly (inputs refreshed between
+    replays, eager work and synchronisation in between)."""
+    import torch
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    for i, (M, K) in enumerate(((8, 25600), (2, 5120), (8, 12288), (1, 512), (5, 8192))):
+        note(f"act quant reuse M={M} K={K}")
+        x = activations_bf16(3, i, M, K)
+        q = nv.quantize_act(to_dev_bf16(x), ws=ws)
+        _sync()
+        _assert_act_equal(q, bf16_to_f32(x))
+        assert _sync_words(ws) == [0, 0, 0, 0]
+    M, K = 8, 12288
+    note(f"act quant graph replay M={M} K={K}")
+    xin = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    xin.copy_(to_dev_bf16(activations_bf16(3, 0, M, K)))
+    q = nv.empty_act(M, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.quantize_act(xin, out=q, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        nv.quantize_act(xin, out=q, ws=ws)
+    for r in range(4):
+        x = activations_bf16(4, 20 + r, M, K, "student_t" if r % 2 else "outlier")
+        xin.copy_(to_dev_bf16(x))
+        torch.empty(1 << 20, device="cuda").fill_(1.0)         # eager work between replays
+        _sync()
+        g.replay()
+        _sync()
+        _assert_act_equal(q, bf16_to_f32(x))
+        assert _sync_words(ws) == [0, 0, 0, 0]
+
+
 def _check_weight(nv, w16, rows=None):
     import torch
     N, K = w16.shape
