@@ -178,6 +178,39 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
                                 uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Fused quantizers of the layer stack (one decode step of a decoder: the
+ * pages' end-to-end measurement runs the NVFP4 linears of whole layers, "ReSET"
+ * GitHub README, "Results"; the stack between the linears is this library's
+ * stand-in for the parts of a layer that are not linears).  Each computes a
+ * binary32 h from a bf16 input and applies the activation quantizer Q above to
+ * h (the tensor maximum over all M x K values of h; the quantizer steps are
+ * the same, starting from binary32 instead of bf16 values):
+ *   rmsnorm:  h[m][k] = x[m][k] * (1 / sqrt(mean_k(x[m][k]^2) + eps)), the
+ *             sum of squares in binary32 in a fixed order, every other step
+ *             one correctly rounded binary32 operation (unweighted RMS norm);
+ *   silu_mul: h[m][k] = (g / (1 + exp(-g))) * u with g = gu[m][k], u =
+ *             gu[m][K + k] (first half gate, second half up), exp from the
+ *             device math library (within a few ulp), the rest correctly
+ *             rounded binary32.
+ *   x_bf16 / gu_bf16  [M][ld] bf16, 1 <= M <= 8, 16 <= K <= 32768, K % 16 == 0,
+ *            ld >= K (rmsnorm) or >= 2K (silu_mul), ld % 8 == 0, 16-byte
+ *            aligned base
+ *   codes/scales/gscale as for nvfp4_quantize_act
+ *   h_out    optional (NULL: not written) binary32 [M][K], 16-byte aligned:
+ *            the h that was quantized
+ *   workspace at least 16 bytes when M > 1 (the same zero-initialised record
+ *            nvfp4_quantize_act uses; it is left zero).
+ * One workgroup per row; the rows' maxima are combined as in
+ * nvfp4_quantize_act. */
+nvfp4_status nvfp4_rmsnorm_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                        float eps, uint8_t* x_codes, uint8_t* x_scales,
+                                        float* x_gscale, float* h_out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+nvfp4_status nvfp4_silu_mul_quantize_act(const uint16_t* gu_bf16, int M, int64_t K, int64_t ldgu,
+                                         uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                         float* h_out, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Workspace bytes nvfp4_linear needs for this shape under the current
  * options: 0 when K is not split, else a fixed 64 KiB region of split-K
  * arrival counters (one per 32-row tile) followed by the binary32 partial
@@ -205,6 +238,63 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
                           const uint8_t* x_scales, const float* x_gscale, const uint8_t* w_codes,
                           const uint8_t* w_scales, const float* w_gscale, void* y, int out_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layer stack: one decode step of an L-layer stack of NVFP4 linears at M
+ * rows, captured once into a HIP graph and replayed (the pages' end-to-end
+ * measurement is whole decode steps replayed as a graph: "ReSET" GitHub
+ * README, "Results").  Per layer, in stream order:
+ *   RMS norm + quantize (nvfp4_rmsnorm_quantize_act) -> QKV linear
+ *   -> quantize the first q_cols columns of its output -> O linear
+ *   -> RMS norm + quantize -> gate_up linear (2 * ffn outputs)
+ *   -> SiLU * mul + quantize (nvfp4_silu_mul_quantize_act) -> down linear,
+ * whose output is the next layer's input.  Every linear writes bf16.  The
+ * stack has no attention, residual or norm weights (out of scope: only the
+ * linears and the quantizers between them are modelled).
+ */
+typedef struct nvfp4_stack nvfp4_stack;
+
+/* One device-tiled weight (as written by nvfp4_quantize_weight). */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+} nvfp4_weight;
+
+typedef struct {
+  int M;            /* activation rows, 1..8                                   */
+  int layers;       /* 1..4096                                                 */
+  int64_t hidden;   /* model width: K of QKV and gate_up, N of O and down      */
+  int64_t qkv_n;    /* N of QKV (>= q_cols, multiple of 8)                     */
+  int64_t q_cols;   /* leading QKV output columns that feed O (K of O)         */
+  int64_t ffn;      /* gate_up has 2 * ffn outputs (gate first); K of down     */
+  float eps;        /* RMS norm epsilon, 0 <= eps < 1                          */
+} nvfp4_stack_config;
+
+/* Create a stack: weights[4 * l + j] is layer l's QKV (j = 0, qkv_n x hidden),
+ * O (1, hidden x q_cols), gate_up (2, 2 ffn x hidden), down (3, hidden x ffn);
+ * hidden, q_cols and ffn are multiples of 16 up to 32768.
+ *   x_in   bf16 [M][hidden], 16-byte aligned: the step's input
+ *   y_out  bf16 [M][hidden]: the last layer's down output
+ * The caller keeps the weights, x_in and y_out alive and in place while the
+ * stack exists (the graph holds their addresses).  `stream` must be a created
+ * stream, not the null stream (capture needs one).  Allocates the
+ * intermediate activations and a workspace (the only allocations), runs one
+ * step eagerly on `stream` (x_in must hold finite values), then captures the
+ * step into a graph on `stream`.  On error nothing is left allocated and
+ * *out is NULL. */
+nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weight* weights,
+                                const uint16_t* x_in, uint16_t* y_out, void* stream,
+                                nvfp4_stack** out);
+
+/* Replay the captured step `steps` times on `stream` (asynchronous). */
+nvfp4_status nvfp4_stack_run(nvfp4_stack* s, int steps, void* stream);
+
+/* The same step launched kernel by kernel, without the graph. */
+nvfp4_status nvfp4_stack_run_eager(nvfp4_stack* s, void* stream);
+
+/* Free the stack's buffers and graph (after the work using them is done). */
+nvfp4_status nvfp4_stack_destroy(nvfp4_stack* s);
 
 #ifdef __cplusplus
 }

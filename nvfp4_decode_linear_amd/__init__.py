@@ -52,6 +52,10 @@ _unpack_weight = _sig("nvfp4_unpack_weight", _c_int, _vp, _vp, _c_i64, _c_i64, _
 _quantize_act = _sig("nvfp4_quantize_act", _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
                      _vp, _c_size, _vp)
 _act_workspace_bytes = _sig("nvfp4_act_workspace_bytes", _c_size, _c_int, _c_i64)
+_rmsnorm_quantize_act = _sig("nvfp4_rmsnorm_quantize_act", _c_int, _vp, _c_int, _c_i64, _c_i64,
+                             ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _c_size, _vp)
+_silu_mul_quantize_act = _sig("nvfp4_silu_mul_quantize_act", _c_int, _vp, _c_int, _c_i64, _c_i64,
+                              _vp, _vp, _vp, _vp, _vp, _c_size, _vp)
 _linear_workspace_bytes = _sig("nvfp4_linear_workspace_bytes", _c_size, _c_int, _c_i64, _c_i64)
 _workspace_init = _sig("nvfp4_workspace_init", _c_int, _vp, _c_size, _vp)
 _linear = _sig("nvfp4_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -191,6 +195,116 @@ def quantize_act(x, out: QuantAct | None = None, ws=None) -> QuantAct:
     _check(_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q.codes), _ptr(q.scales),
                          _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(x)), "nvfp4_quantize_act")
     return q
+
+
+def _nullable(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def rmsnorm_quantize_act(x, eps=1e-6, out: QuantAct | None = None, h_out=None, ws=None):
+    """Unweighted per-row RMS norm of bf16 x [M][K] in binary32, then the
+    activation quantizer on it; h_out (float32 [M][K]) receives h if given."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    q = out if out is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(1, 1, 16, x.device)
+    _check(_rmsnorm_quantize_act(_ptr(x), M, K, x.stride(0), float(eps), _ptr(q.codes),
+                                 _ptr(q.scales), _ptr(q.gscale), _nullable(h_out), _ptr(ws),
+                                 ws.numel(), _stream(x)), "nvfp4_rmsnorm_quantize_act")
+    return q
+
+
+def silu_mul_quantize_act(gu, out: QuantAct | None = None, h_out=None, ws=None):
+    """h = silu(gate) * up from bf16 gu [M][2K] (first half gate), in
+    binary32, then the activation quantizer on it."""
+    torch = _torch()
+    if gu.dtype != torch.bfloat16 or gu.dim() != 2 or gu.stride(1) != 1 or gu.shape[1] % 2:
+        raise ValueError("gu must be a 2-D bf16 tensor [M][2K] with unit column stride")
+    M, K = gu.shape[0], gu.shape[1] // 2
+    q = out if out is not None else empty_act(M, K, gu.device)
+    if ws is None:
+        ws = workspace(1, 1, 16, gu.device)
+    _check(_silu_mul_quantize_act(_ptr(gu), M, K, gu.stride(0), _ptr(q.codes), _ptr(q.scales),
+                                  _ptr(q.gscale), _nullable(h_out), _ptr(ws), ws.numel(),
+                                  _stream(gu)), "nvfp4_silu_mul_quantize_act")
+    return q
+
+
+class _StackConfig(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int), ("layers", ctypes.c_int), ("hidden", ctypes.c_int64),
+                ("qkv_n", ctypes.c_int64), ("q_cols", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("eps", ctypes.c_float)]
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p)]
+
+
+_stack_create = _sig("nvfp4_stack_create", _c_int, ctypes.POINTER(_StackConfig),
+                     ctypes.POINTER(_Weight), _vp, _vp, _vp, ctypes.POINTER(_vp))
+_stack_run = _sig("nvfp4_stack_run", _c_int, _vp, _c_int, _vp)
+_stack_run_eager = _sig("nvfp4_stack_run_eager", _c_int, _vp, _vp)
+_stack_destroy = _sig("nvfp4_stack_destroy", _c_int, _vp)
+
+
+class Stack:
+    """Graph-replayed decode step of a layer stack (nvfp4_stack_*).
+
+    layers: list of (qkv, o, gate_up, down) QuantWeight per layer.  x_in and
+    y_out are bf16 [M][hidden] tensors the caller keeps alive.  The stack
+    captures and replays on its own side stream; run() orders it after the
+    caller's current stream and the caller's stream after it."""
+
+    def __init__(self, M, hidden, qkv_n, q_cols, ffn, layers, x_in, y_out, eps=1e-6):
+        torch = _torch()
+        self._torch = torch
+        self._h = None
+        self.cfg = _StackConfig(M, len(layers), hidden, qkv_n, q_cols, ffn, eps)
+        arr = (_Weight * (4 * len(layers)))()
+        for l, ws4 in enumerate(layers):
+            for j, w in enumerate(ws4):
+                arr[4 * l + j] = _Weight(w.codes.data_ptr(), w.scales.data_ptr(),
+                                         w.gscale.data_ptr())
+        self._keep = (layers, x_in, y_out)
+        self.device = x_in.device
+        self.stream = torch.cuda.Stream(device=self.device)
+        self.stream.wait_stream(torch.cuda.current_stream(self.device))
+        h = _vp()
+        _check(_stack_create(ctypes.byref(self.cfg), arr, _ptr(x_in), _ptr(y_out),
+                             _vp(self.stream.cuda_stream), ctypes.byref(h)),
+               "nvfp4_stack_create")
+        self._h = h
+        torch.cuda.current_stream(self.device).wait_stream(self.stream)
+
+    def _around(self, fn):
+        cur = self._torch.cuda.current_stream(self.device)
+        self.stream.wait_stream(cur)
+        fn()
+        cur.wait_stream(self.stream)
+
+    def run(self, steps=1):
+        self._around(lambda: _check(_stack_run(self._h, int(steps), _vp(self.stream.cuda_stream)),
+                                    "nvfp4_stack_run"))
+
+    def run_eager(self):
+        self._around(lambda: _check(_stack_run_eager(self._h, _vp(self.stream.cuda_stream)),
+                                    "nvfp4_stack_run_eager"))
+
+    def close(self):
+        if self._h:
+            self._torch.cuda.synchronize(self.device)
+            _check(_stack_destroy(self._h), "nvfp4_stack_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 _WS = {}

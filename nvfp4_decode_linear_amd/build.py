@@ -40,9 +40,7 @@ def sources():
 
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
-    if src.endswith(".hip"):
-        cmd[1:1] = DEVICE
+    cmd = [hipcc, *DEVICE, *COMMON, "-c", src, "-o", obj]
     subprocess.run(cmd, check=True)
     return obj
 

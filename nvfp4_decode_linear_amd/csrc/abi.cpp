@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/nvfp4.h"
@@ -30,6 +31,15 @@ nvfp4_status hip_fail(hipError_t e) {
   t_last_hip = (int)e;
   return NVFP4_ERR_HIP;
 }
+
+}  // namespace
+
+namespace nvfp4 {
+// for the other host translation units of the library (stack.cpp)
+nvfp4_status record_hip_error(hipError_t e) { return hip_fail(e); }
+}  // namespace nvfp4
+
+namespace {
 
 // Current device must be a gfx950; cached per device.
 nvfp4_status check_device() {
@@ -303,6 +313,48 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
       x_bf16, M, (int)K, ldx, x_codes, x_scales, x_gscale, static_cast<uint32_t*>(workspace),
       (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(), (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+namespace {
+
+nvfp4_status prep_quantize(int mode, const uint16_t* x, int M, int64_t K, int64_t ld, int64_t ld_min,
+                           float eps, uint8_t* codes, uint8_t* scales, float* gscale, float* h_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (!x || !codes || !scales || !gscale) return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || K < 16 || K % 16 != 0 || K > nvfp4::kPrepMaxK || ld < ld_min || ld % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gscale, 4) ||
+      (h_out && !aligned(h_out, 16)))
+    return NVFP4_ERR_INVALID_ARG;
+  if (M > 1) {
+    if (!workspace || !aligned(workspace, 16)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < nvfp4::kActSyncBytes) return NVFP4_ERR_WORKSPACE;
+  }
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_prep_quantize(
+      mode, x, M, (int)K, ld, eps, codes, scales, gscale, h_out, static_cast<uint32_t*>(workspace),
+      (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(), (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_rmsnorm_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                        float eps, uint8_t* x_codes, uint8_t* x_scales,
+                                        float* x_gscale, float* h_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return prep_quantize(0, x_bf16, M, K, ldx, K, eps, x_codes, x_scales, x_gscale, h_out, workspace,
+                       workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_silu_mul_quantize_act(const uint16_t* gu_bf16, int M, int64_t K, int64_t ldgu,
+                                         uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                         float* h_out, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return prep_quantize(1, gu_bf16, M, K, ldgu, 2 * K, 0.0f, x_codes, x_scales, x_gscale, h_out,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {

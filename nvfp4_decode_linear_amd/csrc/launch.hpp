@@ -63,6 +63,13 @@ hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uin
                                uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
                                hipStream_t s);
 
+// Fused stack quantizers (mode 0: RMS norm, 1: SiLU * mul), one workgroup
+// per row of up to 2 * 1024 blocks, K <= kPrepMaxK.
+constexpr int64_t kPrepMaxK = 32768;
+hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64_t ldx, float eps,
+                                uint8_t* codes, uint8_t* scales, float* gscale, float* h_out,
+                                uint32_t* sync, uint32_t spin_limit, hipStream_t s);
+
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                   uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s);
 

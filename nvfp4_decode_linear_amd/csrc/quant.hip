@@ -87,6 +87,46 @@ __device__ uint32_t tensor_amax_bits(const uint16_t* x, int M, int K, int64_t ld
   return block_reduce_max(amax, red);
 }
 
+constexpr uint32_t kGaveUp = 0xFFFFFFFFu;
+
+// Tensor maximum over the workgroups of the grid: each passes the maximum of
+// its part (a non-negative binary32 or bf16 magnitude pattern; these order
+// like integers) and gets back the maximum over all of them, or kGaveUp if
+// it stopped polling (then it must compute the maximum alone).  Called by all
+// threads of every workgroup; thread 0 talks to the sync record.
+__device__ uint32_t combine_amax(uint32_t amax, uint32_t* sync, uint32_t spin_limit,
+                                 uint32_t* shared_slot) {
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x;
+    __hip_atomic_fetch_max(sync, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t all = kGaveUp;
+    for (uint32_t i = 0;; ++i) {
+      const uint32_t c = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c >= G) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        all = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      if (i + 1 >= spin_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *shared_slot = all;
+    // depart (the amax load above has returned: its value is in `all`)
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t d =
+        __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == G - 1) {                             // every workgroup has read: reset
+      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  return *shared_slot;
+}
+
 template <int BPT>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
@@ -111,36 +151,8 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   amax = block_reduce_max(amax, red);
 
   if (gridDim.x > 1) {
-    if (threadIdx.x == 0) {
-      const uint32_t G = gridDim.x;
-      __hip_atomic_fetch_max(sync, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t all = 0xFFFFFFFFu;                 // "gave up"
-      for (uint32_t i = 0;; ++i) {
-        const uint32_t c = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (c >= G) {
-          __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          all = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        if (i + 1 >= spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      shared_amax = all;
-      // depart (the amax load above has returned: its value is in `all`)
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      const uint32_t d = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      if (d == G - 1) {                           // every workgroup has read: reset
-        __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    amax = shared_amax;
-    if (amax == 0xFFFFFFFFu) amax = tensor_amax_bits(x, M, K, ldx, red);
+    amax = combine_amax(amax, sync, spin_limit, &shared_amax);
+    if (amax == kGaveUp) amax = tensor_amax_bits(x, M, K, ldx, red);
   }
 
   const float sg = tensor_scale(bf16_to_f32(amax));
@@ -152,6 +164,150 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
       const int m = b / nbr, j = b - m * nbr;
       store_block(codes, scales, K, m, j, quantize_block_bf16(v[r], sg));
     }
+  }
+}
+
+// ------------------------------------------------- fused stack quantizers
+//
+// The activation quantizer applied to a binary32 h computed in the same
+// kernel from the previous linear's bf16 output (the layer stack between its
+// linears): h = x / sqrt(mean(x^2) + eps) per row (unweighted RMS norm), or
+// h = silu(g) * u with g, u the two halves of a gate_up row.  One workgroup
+// of 1024 threads per row; thread t owns blocks t, t + 1024, ... of the row
+// and keeps their h in registers through the tensor-amax combine.  h may be
+// written out (binary32) for checking.
+constexpr int kPrepThreads = 1024;
+enum PrepMode { kPrepRms = 0, kPrepSilu = 1 };
+
+__device__ inline void load16_bf16_f32(const uint16_t* p, float (&h)[16]) {
+  uint32_t v[8];
+  load_block_bf16(p, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[2 * i] = __uint_as_float(v[i] << 16);
+    h[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+// sum over the workgroup in a fixed order (the same on every run and in
+// every workgroup that computes it)
+__device__ inline float block_sum_f32(float v, float* red) {
+  v = wave_sum_f32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float all = red[0];
+#pragma unroll
+  for (int w = 1; w < kPrepThreads / kWave; ++w) all += red[w];
+  __syncthreads();
+  return all;
+}
+
+// h of this thread's blocks of row `row` (blocks past the row are zero)
+template <int MODE, int BPT>
+__device__ inline void prep_row(const uint16_t* row, int K, float eps, float (&h)[BPT][16],
+                                float* red) {
+  const int nbr = K >> 4;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int j = min((int)threadIdx.x + r * kPrepThreads, nbr - 1);
+    if constexpr (MODE == kPrepSilu) {
+      float u[16];
+      load16_bf16_f32(row + 16 * j, h[r]);
+      load16_bf16_f32(row + K + 16 * j, u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float g = h[r][i];
+        const float sig = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
+        h[r][i] = __fmul_rn(sig, u[i]);
+      }
+    } else {
+      load16_bf16_f32(row + 16 * j, h[r]);
+    }
+    if ((int)threadIdx.x + r * kPrepThreads >= nbr) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[r][i] = 0.0f;
+    }
+  }
+  if constexpr (MODE == kPrepRms) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = __fadd_rn(ss, __fmul_rn(h[r][i], h[r][i]));
+    const float ms = __fdiv_rn(block_sum_f32(ss, red), (float)K);
+    const float rinv = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, eps)));
+#pragma unroll
+    for (int r = 0; r < BPT; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[r][i] = __fmul_rn(h[r][i], rinv);
+  }
+}
+
+template <int BPT>
+__device__ inline uint32_t amax_bits_f32(const float (&h)[BPT][16]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(h[r][i]) & 0x7FFFFFFFu);
+  return m;
+}
+
+template <int MODE, int BPT>
+__global__ __launch_bounds__(kPrepThreads) void prep_quant_kernel(
+    const uint16_t* __restrict__ x, int K, int64_t ldx, float eps, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, float* __restrict__ h_out,
+    uint32_t* sync, uint32_t spin_limit) {
+  __shared__ float red[kPrepThreads / kWave];
+  __shared__ uint32_t shared_amax;
+  const int m = blockIdx.x;
+  const int nbr = K >> 4;
+  float h[BPT][16];
+  prep_row<MODE, BPT>(x + (int64_t)m * ldx, K, eps, h, red);
+  if (h_out) {
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int j = (int)threadIdx.x + r * kPrepThreads;
+      if (j < nbr) {
+        float4* o = reinterpret_cast<float4*>(h_out + (int64_t)m * K + 16 * j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = make_float4(h[r][4 * q], h[r][4 * q + 1], h[r][4 * q + 2], h[r][4 * q + 3]);
+      }
+    }
+  }
+  uint32_t amax = wave_max_u32(amax_bits_f32<BPT>(h));
+  if ((threadIdx.x & 63) == 0) reinterpret_cast<uint32_t*>(red)[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = 0;
+#pragma unroll
+  for (int w = 0; w < kPrepThreads / kWave; ++w)
+    amax = max(amax, reinterpret_cast<uint32_t*>(red)[w]);
+  __syncthreads();
+  if (gridDim.x > 1) {
+    amax = combine_amax(amax, sync, spin_limit, &shared_amax);
+    if (amax == kGaveUp) {                        // every row's h, this workgroup alone
+      amax = 0;
+      for (int mm = 0; mm < (int)gridDim.x; ++mm) {
+        float hh[BPT][16];
+        prep_row<MODE, BPT>(x + (int64_t)mm * ldx, K, eps, hh, red);
+        amax = max(amax, amax_bits_f32<BPT>(hh));
+      }
+      amax = wave_max_u32(amax);
+      if ((threadIdx.x & 63) == 0) reinterpret_cast<uint32_t*>(red)[threadIdx.x >> 6] = amax;
+      __syncthreads();
+      amax = 0;
+#pragma unroll
+      for (int w = 0; w < kPrepThreads / kWave; ++w)
+        amax = max(amax, reinterpret_cast<uint32_t*>(red)[w]);
+    }
+  }
+  const float sg = tensor_scale(__uint_as_float(amax));
+  if (m == 0 && threadIdx.x == 0) *gscale = sg;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int j = (int)threadIdx.x + r * kPrepThreads;
+    if (j < nbr) store_block(codes, scales, K, m, j, quantize_block_f32(h[r], sg));
   }
 }
 
@@ -288,6 +444,28 @@ hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uin
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+int prep_bpt(int64_t K) { return (K >> 4) <= kPrepThreads ? 1 : 2; }
+
+hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64_t ldx, float eps,
+                                uint8_t* codes, uint8_t* scales, float* gscale, float* h_out,
+                                uint32_t* sync, uint32_t spin_limit, hipStream_t s) {
+  const uint32_t spin = spin_limit ? spin_limit : kActDefaultSpin;
+  const dim3 g(M), b(kPrepThreads);
+#define NVFP4_PREP(MODE, BPT)                                                                  \
+  hipLaunchKernelGGL((prep_quant_kernel<MODE, BPT>), g, b, 0, s, x, K, ldx, eps, codes, scales, \
+                     gscale, h_out, sync, spin)
+  const int bpt = prep_bpt(K);
+  if (mode == kPrepRms) {
+    if (bpt == 1) NVFP4_PREP(kPrepRms, 1);
+    else NVFP4_PREP(kPrepRms, 2);
+  } else {
+    if (bpt == 1) NVFP4_PREP(kPrepSilu, 1);
+    else NVFP4_PREP(kPrepSilu, 2);
+  }
+#undef NVFP4_PREP
   return hipGetLastError();
 }
 

@@ -1,0 +1,200 @@
+// Layer-stack driver: one decode step of an L-layer stack of NVFP4 linears
+// captured once into a HIP graph and replayed ("ReSET" GitHub README,
+// "Results": the end-to-end figures are decode steps of a whole model, with
+// the step replayed as a graph).  Per layer, in stream order:
+//
+//   x -> RMS norm + quantize -> QKV -> quantize (first q_cols columns)
+//     -> O -> RMS norm + quantize -> gate_up -> SiLU * mul + quantize
+//     -> down -> x of the next layer
+//
+// Every linear writes bf16.  There is no attention, residual or weighted
+// norm: the stack exercises the linears and the quantizers between them at
+// the model's shapes, the rest of a layer is out of scope.  The graph holds
+// kernel nodes only (the workspace is zeroed once, before capture, by a fill
+// kernel; the split-K counters and the quantizer's sync record reset
+// themselves), so replays need no host work.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+nvfp4_status record_hip_error(hipError_t e);   // abi.cpp: keeps nvfp4_last_hip_error
+}
+
+struct nvfp4_stack {
+  nvfp4_stack_config cfg;
+  std::vector<nvfp4_weight> w;          // [layers][4]
+  int device = -1;
+  const uint16_t* x_in = nullptr;       // [M][hidden] (the caller's)
+  uint16_t* y_out = nullptr;            // [M][hidden] (the caller's)
+  // device buffers (owned)
+  uint16_t* h = nullptr;                // [M][hidden] inter-layer activation
+  uint16_t* qkv = nullptr;              // [M][qkv_n]
+  uint16_t* o = nullptr;                // [M][hidden]
+  uint16_t* gu = nullptr;               // [M][2 ffn]
+  uint8_t* a_codes = nullptr;           // [M][kmax / 2]
+  uint8_t* a_scales = nullptr;          // [M][kmax / 16]
+  float* a_gscale = nullptr;            // 1 float (padded to 256 B)
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+enum { kQkv = 0, kO = 1, kGateUp = 2, kDown = 3 };
+
+nvfp4_status hip_err(hipError_t e) { return nvfp4::record_hip_error(e); }
+
+void free_all(nvfp4_stack* s) {
+  if (s->exec) (void)hipGraphExecDestroy(s->exec);
+  if (s->graph) (void)hipGraphDestroy(s->graph);
+  void* bufs[] = {s->h, s->qkv, s->o, s->gu, s->a_codes, s->a_scales, s->a_gscale, s->ws};
+  for (void* p : bufs)
+    if (p) (void)hipFree(p);
+}
+
+// One decode step, enqueued on `st` (eagerly or under capture).
+nvfp4_status enqueue_step(nvfp4_stack* s, void* st) {
+  const nvfp4_stack_config& c = s->cfg;
+  const int M = c.M;
+  nvfp4_status r = NVFP4_OK;
+  auto lin = [&](const nvfp4_weight& w, int64_t N, int64_t K, void* y) {
+    return nvfp4_linear(M, N, K, s->a_codes, s->a_scales, s->a_gscale, w.codes, w.scales,
+                        w.gscale, y, NVFP4_OUT_BF16, s->ws, s->ws_bytes, st);
+  };
+  for (int l = 0; l < c.layers && r == NVFP4_OK; ++l) {
+    const nvfp4_weight* w = &s->w[(size_t)l * 4];
+    const uint16_t* xin = l == 0 ? s->x_in : s->h;
+    uint16_t* xout = l == c.layers - 1 ? s->y_out : s->h;
+    if ((r = nvfp4_rmsnorm_quantize_act(xin, M, c.hidden, c.hidden, c.eps, s->a_codes, s->a_scales,
+                                        s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) != NVFP4_OK)
+      break;
+    if ((r = lin(w[kQkv], c.qkv_n, c.hidden, s->qkv)) != NVFP4_OK) break;
+    if ((r = nvfp4_quantize_act(s->qkv, M, c.q_cols, c.qkv_n, s->a_codes, s->a_scales,
+                                s->a_gscale, s->ws, s->ws_bytes, st)) != NVFP4_OK)
+      break;
+    if ((r = lin(w[kO], c.hidden, c.q_cols, s->o)) != NVFP4_OK) break;
+    if ((r = nvfp4_rmsnorm_quantize_act(s->o, M, c.hidden, c.hidden, c.eps, s->a_codes,
+                                        s->a_scales, s->a_gscale, nullptr, s->ws, s->ws_bytes,
+                                        st)) != NVFP4_OK)
+      break;
+    if ((r = lin(w[kGateUp], 2 * c.ffn, c.hidden, s->gu)) != NVFP4_OK) break;
+    if ((r = nvfp4_silu_mul_quantize_act(s->gu, M, c.ffn, 2 * c.ffn, s->a_codes, s->a_scales,
+                                         s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) !=
+        NVFP4_OK)
+      break;
+    r = lin(w[kDown], c.hidden, c.ffn, xout);
+  }
+  return r;
+}
+
+bool valid_config(const nvfp4_stack_config& c) {
+  auto ok_dim = [](int64_t v) { return v >= 16 && v % 16 == 0 && v <= 32768; };
+  return c.M >= 1 && c.M <= 8 && c.layers >= 1 && c.layers <= 4096 && ok_dim(c.hidden) &&
+         ok_dim(c.q_cols) && ok_dim(c.ffn) && c.qkv_n >= c.q_cols && c.qkv_n % 8 == 0 &&
+         c.qkv_n <= (int64_t(1) << 20) && c.eps >= 0.0f && c.eps < 1.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weight* weights,
+                                const uint16_t* x_in, uint16_t* y_out, void* stream,
+                                nvfp4_stack** out) {
+  if (!out) return NVFP4_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!cfg || !weights || !x_in || !y_out || !stream) return NVFP4_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x_in) % 16 || reinterpret_cast<uintptr_t>(y_out) % 4)
+    return NVFP4_ERR_INVALID_ARG;
+  if (cfg->M > 8) return NVFP4_ERR_UNSUPPORTED;
+  if (!valid_config(*cfg)) return NVFP4_ERR_INVALID_ARG;
+  for (int i = 0; i < cfg->layers * 4; ++i)
+    if (!weights[i].codes || !weights[i].scales || !weights[i].gscale) return NVFP4_ERR_INVALID_ARG;
+  nvfp4_stack* s = new (std::nothrow) nvfp4_stack;
+  if (!s) return NVFP4_ERR_HIP;
+  s->cfg = *cfg;
+  s->w.assign(weights, weights + (size_t)cfg->layers * 4);
+  s->x_in = x_in;
+  s->y_out = y_out;
+  const nvfp4_stack_config& c = s->cfg;
+  const int M = c.M;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  nvfp4_status r = NVFP4_OK;
+  hipError_t e = hipGetDevice(&s->device);
+  const int64_t kmax = std::max({c.hidden, c.q_cols, c.ffn});
+  size_t ws = 256;
+  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.qkv_n, c.hidden));
+  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.q_cols));
+  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, 2 * c.ffn, c.hidden));
+  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.ffn));
+  s->ws_bytes = ws;
+  auto alloc = [&](auto** p, size_t bytes) {
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(bytes, 256));
+  };
+  alloc(&s->h, (size_t)M * c.hidden * 2);
+  alloc(&s->qkv, (size_t)M * c.qkv_n * 2);
+  alloc(&s->o, (size_t)M * c.hidden * 2);
+  alloc(&s->gu, (size_t)M * 2 * c.ffn * 2);
+  alloc(&s->a_codes, (size_t)M * kmax / 2);
+  alloc(&s->a_scales, (size_t)M * kmax / 16);
+  alloc(&s->a_gscale, 256);
+  alloc(&s->ws, ws);
+  if (e != hipSuccess) {
+    r = hip_err(e);
+  } else if ((r = nvfp4_workspace_init(s->ws, ws, st)) == NVFP4_OK) {
+    // one eager step (validates every call and initialises the kernels'
+    // attributes), then the capture
+    r = enqueue_step(s, st);
+    if (r == NVFP4_OK && (e = hipStreamSynchronize(st)) != hipSuccess) r = hip_err(e);
+    if (r == NVFP4_OK) {
+      if ((e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+        r = hip_err(e);
+      } else {
+        const nvfp4_status rc = enqueue_step(s, st);
+        e = hipStreamEndCapture(st, &s->graph);
+        if (rc != NVFP4_OK) r = rc;
+        else if (e != hipSuccess) r = hip_err(e);
+        else if ((e = hipGraphInstantiate(&s->exec, s->graph, nullptr, nullptr, 0)) != hipSuccess)
+          r = hip_err(e);
+      }
+    }
+  }
+  if (r != NVFP4_OK) {
+    free_all(s);
+    delete s;
+    return r;
+  }
+  *out = s;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_stack_run(nvfp4_stack* s, int steps, void* stream) {
+  if (!s || steps < 0) return NVFP4_ERR_INVALID_ARG;
+  for (int i = 0; i < steps; ++i) {
+    const hipError_t e = hipGraphLaunch(s->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e);
+  }
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_stack_run_eager(nvfp4_stack* s, void* stream) {
+  if (!s) return NVFP4_ERR_INVALID_ARG;
+  return enqueue_step(s, stream);
+}
+
+nvfp4_status nvfp4_stack_destroy(nvfp4_stack* s) {
+  if (!s) return NVFP4_ERR_INVALID_ARG;
+  free_all(s);
+  delete s;
+  return NVFP4_OK;
+}
+
+}  // extern "C"

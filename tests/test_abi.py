@@ -183,3 +183,56 @@ def test_no_device_is_reported(lib, no_gpu):
     assert lib.nvfp4_quantize_act(FAKE, 1, 512, 512, FAKE, FAKE, FAKE, None, 0, None) == 3
     assert lib.nvfp4_linear(1, 256, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
                             1 << 20, None) == 3
+
+
+def test_stack_argument_errors(lib, no_gpu):
+    class Cfg(ctypes.Structure):
+        _fields_ = [("M", ctypes.c_int), ("layers", ctypes.c_int), ("hidden", ctypes.c_int64),
+                    ("qkv_n", ctypes.c_int64), ("q_cols", ctypes.c_int64),
+                    ("ffn", ctypes.c_int64), ("eps", ctypes.c_float)]
+
+    class W(ctypes.Structure):
+        _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                    ("gscale", ctypes.c_void_p)]
+
+    vp = ctypes.c_void_p
+    f = lib.nvfp4_stack_create
+    f.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(W), vp, vp, vp, ctypes.POINTER(vp)]
+    ws = (W * 8)(*[W(0x1000, 0x1000, 0x1000)] * 8)
+    out = vp(0x1234)
+    good = Cfg(1, 2, 512, 768, 512, 1024, 1e-6)
+    assert f(None, ws, FAKE, FAKE, FAKE, ctypes.byref(out)) == 1 and out.value is None
+    assert f(ctypes.byref(good), ws, FAKE, FAKE, None, ctypes.byref(out)) == 1   # null stream
+    assert f(ctypes.byref(good), ws, None, FAKE, FAKE, ctypes.byref(out)) == 1
+    assert f(ctypes.byref(good), ws, ctypes.c_void_p(0x1008), FAKE, FAKE,
+             ctypes.byref(out)) == 1                                             # x_in alignment
+    for bad in (Cfg(9, 2, 512, 768, 512, 1024, 1e-6),):
+        assert f(ctypes.byref(bad), ws, FAKE, FAKE, FAKE, ctypes.byref(out)) == 2
+    for bad in (Cfg(0, 2, 512, 768, 512, 1024, 1e-6), Cfg(1, 0, 512, 768, 512, 1024, 1e-6),
+                Cfg(1, 2, 520, 768, 512, 1024, 1e-6), Cfg(1, 2, 512, 500, 512, 1024, 1e-6),
+                Cfg(1, 2, 512, 768, 512, 40000, 1e-6), Cfg(1, 2, 512, 768, 512, 1024, -1.0)):
+        assert f(ctypes.byref(bad), ws, FAKE, FAKE, FAKE, ctypes.byref(out)) == 1
+    nulls = (W * 8)(*[W(0x1000, 0x1000, 0x1000)] * 7 + [W(0x1000, 0, 0x1000)])
+    assert f(ctypes.byref(good), nulls, FAKE, FAKE, FAKE, ctypes.byref(out)) == 1
+    lib.nvfp4_stack_run.argtypes = [vp, ctypes.c_int, vp]
+    lib.nvfp4_stack_destroy.argtypes = [vp]
+    assert lib.nvfp4_stack_run(None, 1, None) == 1
+    assert lib.nvfp4_stack_destroy(None) == 1
+
+
+def test_fused_quantize_argument_errors(lib, no_gpu):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    r = lib.nvfp4_rmsnorm_quantize_act
+    r.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_float, vp, vp, vp, vp, vp,
+                  ctypes.c_size_t, vp]
+    s = lib.nvfp4_silu_mul_quantize_act
+    s.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    assert r(FAKE, 9, 512, 512, 1e-6, FAKE, FAKE, FAKE, None, FAKE, 64, None) == 2
+    assert r(FAKE, 1, 40960, 40960, 1e-6, FAKE, FAKE, FAKE, None, FAKE, 64, None) == 1  # K cap
+    assert r(FAKE, 1, 512, 512, -1.0, FAKE, FAKE, FAKE, None, FAKE, 64, None) == 1      # eps
+    assert r(FAKE, 2, 512, 512, 1e-6, FAKE, FAKE, FAKE, None, None, 0, None) == 1      # ws
+    assert r(FAKE, 2, 512, 512, 1e-6, FAKE, FAKE, FAKE, None, FAKE, 8, None) == 4
+    assert r(FAKE, 1, 512, 512, 1e-6, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), None, 0,
+             None) == 1                                                             # h_out
+    assert s(FAKE, 1, 512, 1000, FAKE, FAKE, FAKE, None, None, 0, None) == 1        # ld < 2K
+    assert s(FAKE, 1, 512, 1024, FAKE, FAKE, FAKE, None, None, 0, None) == 3        # no device

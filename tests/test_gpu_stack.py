@@ -1,0 +1,167 @@
+"""The layer-stack driver (nvfp4_stack_*): the graph-replayed decode step
+against the same step issued op by op through the C ABI (bit-identical: the
+same kernels in the same order), replays with fresh inputs and eager work in
+between, and, teacher-forced on the first and last layer, every op of the
+step against the oracle (the quantizers bit-exact given their input, the
+linears within the tolerance bound)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import note, to_dev_bf16
+from workloads import activations_bf16, bf16_to_f32, weights_bf16
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+CONFIGS = [  # M, hidden, qkv_n, q_cols, ffn, layers
+    (2, 512, 768, 512, 1024, 3),
+    (1, 256, 384, 256, 512, 2),
+    (8, 512, 640, 384, 768, 2),
+]
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import nvfp4_decode_linear_amd as nv
+    return nv
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _weights(nv, cfg):
+    M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    shapes = [(qkv_n, hidden), (hidden, q_cols), (2 * ffn, hidden), (hidden, ffn)]
+    src, q = [], []
+    for l in range(layers):
+        w16 = [weights_bf16(6, 10 * l + j, N, K) for j, (N, K) in enumerate(shapes)]
+        src.append(w16)
+        q.append(tuple(nv.quantize_weight(to_dev_bf16(w)) for w in w16))
+    return src, q
+
+
+def _eager(nv, cfg, wq, x, trace=False):
+    """The step op by op through the binding; with trace, the inputs and
+    outputs of every op of every layer."""
+    import torch
+    M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    ops = []
+    cur = x
+    for l in range(layers):
+        qkv_w, o_w, gu_w, dn_w = wq[l]
+        h1 = torch.empty((M, hidden), dtype=torch.float32, device="cuda")
+        a1 = nv.rmsnorm_quantize_act(cur, 1e-6, h_out=h1)
+        qkv = nv.linear(a1, qkv_w, out_dtype=torch.bfloat16)
+        a2 = nv.quantize_act(qkv[:, :q_cols])
+        o = nv.linear(a2, o_w, out_dtype=torch.bfloat16)
+        h3 = torch.empty((M, hidden), dtype=torch.float32, device="cuda")
+        a3 = nv.rmsnorm_quantize_act(o, 1e-6, h_out=h3)
+        gu = nv.linear(a3, gu_w, out_dtype=torch.bfloat16)
+        h4 = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
+        a4 = nv.silu_mul_quantize_act(gu, h_out=h4)
+        dn = nv.linear(a4, dn_w, out_dtype=torch.bfloat16)
+        if trace:
+            ops.append(dict(x=cur, h1=h1, a1=a1, qkv=qkv, a2=a2, o=o, h3=h3, a3=a3, gu=gu, h4=h4,
+                            a4=a4, dn=dn))
+        cur = dn
+    return cur, ops
+
+
+def _oracle_act(a):
+    return oracle.NVFP4Tensor(a.codes.cpu().numpy(), a.scales.cpu().numpy(),
+                              np.asarray(a.gscale.cpu().numpy()[0], np.float32))
+
+
+def _check_quant(a, h32):
+    ref = oracle.quantize(h32)
+    assert np.array_equal(a.codes.cpu().numpy(), ref.codes)
+    assert np.array_equal(a.scales.cpu().numpy(), ref.scales)
+    assert a.gscale.cpu().numpy().view(np.uint32)[0] == np.asarray(ref.gscale,
+                                                                   np.float32).view(np.uint32)
+
+
+def _check_linear(y_bf16, a, w16):
+    ow = oracle.quantize(bf16_to_f32(w16))
+    ox = _oracle_act(a)
+    ref = oracle.linear_ref(ox, ow)
+    bound = oracle.tolerance_bound(ox, ow) + 0.5 * np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    got = y_bf16.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_stack_graph_matches_op_by_op(nv, cfg):
+    import torch
+    M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    note(f"stack graph vs eager cfg={cfg}")
+    src, wq = _weights(nv, cfg)
+    x = torch.empty((M, hidden), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, hidden), dtype=torch.bfloat16, device="cuda")
+    x.copy_(to_dev_bf16(activations_bf16(7, 0, M, hidden, "normal")))
+    st = nv.Stack(M, hidden, qkv_n, q_cols, ffn, wq, x, y)
+    try:
+        for r in range(3):
+            x.copy_(to_dev_bf16(activations_bf16(7, r, M, hidden, "normal" if r else "outlier")))
+            torch.empty(1 << 20, device="cuda").fill_(2.0)      # eager work between replays
+            _sync()
+            ref, _ = _eager(nv, cfg, wq, x)
+            _sync()
+            st.run(1)
+            _sync()
+            assert np.array_equal(y.cpu().view(torch.int16).numpy(),
+                                  ref.cpu().view(torch.int16).numpy()), f"replay {r}"
+            y.zero_()
+            st.run_eager()
+            _sync()
+            assert np.array_equal(y.cpu().view(torch.int16).numpy(),
+                                  ref.cpu().view(torch.int16).numpy()), f"eager {r}"
+        st.run(5)                                          # replays back to back
+        _sync()
+        assert np.array_equal(y.cpu().view(torch.int16).numpy(),
+                              ref.cpu().view(torch.int16).numpy())
+    finally:
+        st.close()
+
+
+@pytest.mark.parametrize("cfg", CONFIGS[:2])
+def test_stack_ops_teacher_forced_vs_oracle(nv, cfg):
+    import torch
+    M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    src, wq = _weights(nv, cfg)
+    x = to_dev_bf16(activations_bf16(7, 5, M, hidden, "outlier"))
+    _, ops = _eager(nv, cfg, wq, x, trace=True)
+    _sync()
+    for l in sorted({0, layers - 1}):
+        note(f"stack teacher-forced layer {l} cfg={cfg}")
+        t = ops[l]
+        w16 = src[l]
+        xin = bf16_to_f32(t["x"].cpu().view(torch.int16).numpy().view(np.uint16))
+        h1 = t["h1"].cpu().numpy()
+        ref = oracle.rms_norm_rows(xin.astype(np.float64))
+        assert np.all(np.abs(h1 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
+        _check_quant(t["a1"], h1)
+        _check_linear(t["qkv"], t["a1"], w16[0])
+        qs = bf16_to_f32(t["qkv"].cpu().view(torch.int16).numpy().view(np.uint16))[:, :q_cols]
+        _check_quant(t["a2"], qs)
+        _check_linear(t["o"], t["a2"], w16[1])
+        oin = bf16_to_f32(t["o"].cpu().view(torch.int16).numpy().view(np.uint16))
+        h3 = t["h3"].cpu().numpy()
+        ref = oracle.rms_norm_rows(oin.astype(np.float64))
+        assert np.all(np.abs(h3 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
+        _check_quant(t["a3"], h3)
+        _check_linear(t["gu"], t["a3"], w16[2])
+        gin = bf16_to_f32(t["gu"].cpu().view(torch.int16).numpy().view(np.uint16))
+        h4 = t["h4"].cpu().numpy()
+        ref = oracle.silu_mul(gin.astype(np.float64))
+        assert np.all(np.abs(h4 - ref) <= 16 * U32 * np.abs(ref) + 1e-30)
+        _check_quant(t["a4"], h4)
+        _check_linear(t["dn"], t["a4"], w16[3])
