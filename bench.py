@@ -3,23 +3,37 @@
 A step is one pass of the decode hot path over the four projections of a
 Qwen3-8B-shaped decoder layer (QKV 6144x4096, O 4096x4096, gate_up
 24576x4096, down 4096x12288) at M activation rows: for each projection the
-bf16 activation is quantized to NVFP4 on the device and the NVFP4 linear
-streams the FP4 weights.  Weights are quantized once, then copied into
-enough distinct buffers (>= 1 GiB in total) that every step reads weights
-that are not resident in the 256 MB Infinity Cache.  Inputs are seeded
+bf16 activation is quantized to NVFP4 on the device (nvfp4_quantize_act)
+and the NVFP4 linear streams the FP4 weights (nvfp4_linear, binary32 out).
+Weights are quantized once, then copied into enough distinct buffers
+(>= 1.2 GiB) that every step reads weights that are not resident in the
+256 MB Infinity Cache; step i uses copy i mod copies.  Each copy's step is
+captured into a HIP graph and a timed step is one graph replay, so the
+host's launch cost is not part of the measurement.  Inputs are seeded
 synthetic data with the shapes and distributions of that workload.
 
-Prints one JSON line: the step's whole-path algorithmic HBM bytes per
-second (value), the GEMV kernel's roofline fraction (HIP events around each
-GEMV launch on the launch stream, over the timed steps), per-projection
-microseconds and GB/s, and the CPU oracle timed on a bounded sample.
+Prints one JSON line with the step's whole-path algorithmic HBM bytes per
+second (value) and:
+  roofline      the GEMV kernel (gemv_mfma_kernel): algorithmic bytes per
+                launch / its average launch time, from HIP events around
+                replays of GEMV-only graphs on the launch stream; traffic
+                from the committed rocprofv3 counter summary when it was
+                taken on the current kernel source
+  per_linear    GEMV-only us and GB/s per projection at M = 1, 2, 4, 8, and
+                the activation quantizer's us
+  linears_32b   the same for the Qwen3-32B-shaped projections at M = 1, 4, 8
+  stack         one decode step of a 64-layer stack of the 32B projections
+                (graph replayed 1500 times) at M = 1 and 8
+  cpu_baseline  the CPU oracle on a bounded sample of the step
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +44,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 WEIGHT_BYTES_PER_ELEM = 0.5 + 1.0 / 16
+GEMV_KERNEL = "gemv_mfma_kernel"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_kernel_qwen3_8b_m1_pmc.txt")
+GEMV_SOURCES = ["nvfp4_decode_linear_amd/csrc/gemv_stream.hip",
+                "nvfp4_decode_linear_amd/csrc/gemv_common.hpp"]
 
 
 def gemv_bytes(M, N, K, out_bytes=4):
@@ -39,10 +57,18 @@ def gemv_bytes(M, N, K, out_bytes=4):
             + M * N * out_bytes)
 
 
-def actq_bytes(M, K):
-    """Algorithmic bytes of the activation quantizer: bf16 in, codes and
-    scales out (plus the tensor scale)."""
-    return M * K * 2 + M * K * WEIGHT_BYTES_PER_ELEM + 4
+def actq_bytes(M, K, in_bytes=2):
+    """Algorithmic bytes of an activation quantizer: the input read once,
+    codes and scales out (plus the tensor scale)."""
+    return M * K * in_bytes + M * K * WEIGHT_BYTES_PER_ELEM + 4
+
+
+def gemv_source_sha():
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -50,14 +76,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--m", type=int, default=1, help="activation rows (1..8)")
-    ap.add_argument("--workload", default="8b", choices=["8b", "32b"])
+    ap.add_argument("--m", type=int, default=1, help="activation rows of the timed step (1..8)")
     ap.add_argument("--copies-gib", type=float, default=1.2,
                     help="total bytes of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--sweep", action="store_true",
-                    help="also report GEMV-only us and GB/s at M = 1, 2, 4, 8")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed step and its roofline (no M sweep, 32B, stack)")
+    ap.add_argument("--stack-layers", type=int, default=64)
+    ap.add_argument("--stack-steps", type=int, default=1500)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only a 256 MiB device copy and a few GEMV launches of the "
+                         "timed workload (for rocprofv3 counter runs), print nothing else")
     return ap.parse_args()
 
 
@@ -101,11 +131,71 @@ def cpu_baseline(linears, cfg, M, kind, budget_s):
     }
 
 
+def read_traffic(M):
+    """HBM bytes per GEMV launch of the timed workload from the committed
+    counter summary, if it was taken on the current GEMV source (else
+    None): (FETCH_SIZE + WRITE_SIZE) KiB per dispatch, each scaled by the
+    factor that maps the same counter onto a device copy of known size."""
+    if M != 1 or not os.path.exists(TRAFFIC_SUMMARY):
+        return None, "no counter summary for this workload"
+    rec = None
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            m = re.match(r"^TRAFFIC_JSON (.*)$", line.strip())
+            if m:
+                rec = json.loads(m.group(1))
+    if rec is None:
+        return None, "counter summary has no TRAFFIC_JSON line"
+    if rec.get("gemv_source_sha") != gemv_source_sha():
+        return None, "GEMV source changed since the counters were taken"
+    return rec["bytes_per_launch"], (f"rocprofv3 FETCH_SIZE x {rec['fetch_scale']:.3f} + "
+                                     f"WRITE_SIZE x {rec['write_scale']:.3f} per dispatch, mean "
+                                     f"of the step's {rec['launches']} GEMV launches "
+                                     f"(algorithmic {rec['algorithmic_bytes_per_launch']:.0f})")
+
+
+class Timer:
+    """Graph capture and replay timing on one side stream (events recorded on
+    the stream the kernels run on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.Stream()
+
+    def capture(self, fn):
+        torch = self.torch
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            fn()                                   # eager once (lazy init, workspaces)
+        torch.cuda.current_stream().wait_stream(self.stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_replays(self, graphs, n, warm=2):
+        """Average ms of one replay, cycling through `graphs`, n replays."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(warm * len(graphs)):
+                graphs[i % len(graphs)].replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for i in range(n):
+                graphs[i % len(graphs)].replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the decode linear runs on a single MI355X "
-              "(--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this build runs the decode linear on a single "
+              "MI355X only (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -117,101 +207,117 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     M = args.m
-    if args.workload == "8b":
-        linears, cfg, kind, wl = QWEN3_8B, (2 if M == 1 else 3), "outlier", "qwen3_8b_decode_step"
-    else:
-        linears, cfg, kind, wl = QWEN3_32B, 4, "student_t", "qwen3_32b_decode_step"
+    linears, kind = QWEN3_8B, "outlier"
+    cfg = 2 if M == 1 else 3
+    wl = f"qwen3_8b_decode_step_m{M}"
 
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # weights: quantize once, then copy to defeat the Infinity Cache
-    base = []
-    for li, L in enumerate(linears):
-        wq = nv.quantize_weight(to_dev(weights_bf16(cfg, li, L.N, L.K)))
-        base.append(wq)
+    # ---- weights: quantize once, then copy to defeat the Infinity Cache
+    base = [nv.quantize_weight(to_dev(weights_bf16(cfg, li, L.N, L.K)))
+            for li, L in enumerate(linears)]
     set_bytes = sum(w.codes.numel() + w.scales.numel() for w in base)
-    copies = max(1, int(np.ceil(args.copies_gib * (1 << 30) / set_bytes)))
-    wsets = [base]
-    for _ in range(copies - 1):
-        wsets.append([nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N,
-                                     w.K) for w in base])
-    xs = [to_dev(activations_bf16(cfg, li, M, L.K, kind)) for li, L in enumerate(linears)]
+    copies = max(2, int(np.ceil(args.copies_gib * (1 << 30) / set_bytes)))
+    wsets = [base] + [[nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N,
+                                      w.K) for w in base] for _ in range(copies - 1)]
+    xs = [to_dev(activations_bf16(cfg, li, 8, L.K, kind)) for li, L in enumerate(linears)]
+    ws = None
+    for Mx in (1, 2, 4, 8):
+        for L in linears:
+            ws = nv.workspace(Mx, L.N, L.K, dev)
+    torch.cuda.synchronize()
+
+    if args.pmc_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                             # the calibration copy: 256 MiB read + write
+        xq = [nv.quantize_act(xs[li][:M]) for li in range(len(linears))]
+        ys = [torch.empty((M, L.N), dtype=torch.float32, device=dev) for L in linears]
+        for c in range(2):
+            for li in range(len(linears)):
+                nv.linear(xq[li], wsets[c][li], out=ys[li], ws=ws)
+        torch.cuda.synchronize()
+        return
+
+    timer = Timer(torch)
+
+    # ---- the timed step: per projection act quant + linear, one graph per copy
     xqs = [nv.empty_act(M, L.K) for L in linears]
     ys = [torch.empty((M, L.N), dtype=torch.float32, device=dev) for L in linears]
-    ws = nv.workspace(M, max(L.N for L in linears), max(L.K for L in linears))
-    for L in linears:
-        ws = nv.workspace(M, L.N, L.K)
+    x_m = [x[:M] for x in xs]
+
+    def step_fn(c):
+        def fn():
+            for li in range(len(linears)):
+                nv.quantize_act(x_m[li], out=xqs[li], ws=ws)
+                nv.linear(xqs[li], wsets[c][li], out=ys[li], ws=ws)
+        return fn
+
+    step_graphs = [timer.capture(step_fn(c)) for c in range(copies)]
+    with torch.cuda.stream(timer.stream):
+        for i in range(args.warmup):
+            step_graphs[i % copies].replay()
     torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-
-    def step(i, evs=None):
-        wset = wsets[i % copies]
-        for li in range(len(linears)):
-            nv.quantize_act(xs[li], out=xqs[li])
-            if evs is not None:
-                evs[li][0].record(stream)
-            nv.linear(xqs[li], wset[li], out=ys[li], ws=ws)
-            if evs is not None:
-                evs[li][1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in linears] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, ev[i])
-    t_end.record(stream)
+    with torch.cuda.stream(timer.stream):
+        t_start.record(timer.stream)
+        for i in range(args.steps):
+            step_graphs[(args.warmup + i) % copies].replay()
+        t_end.record(timer.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-
-    per = []
-    tot_b = tot_t = 0.0
-    for li, L in enumerate(linears):
-        us = np.mean([ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(args.steps)]) * 1e3
-        b = gemv_bytes(M, L.N, L.K)
-        tot_b += b
-        tot_t += us
-        per.append({"name": L.name, "N": L.N, "K": L.K, "us": round(float(us), 3),
-                    "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                    "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     step_bytes = sum(gemv_bytes(M, L.N, L.K) + actq_bytes(M, L.K) for L in linears)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = tot_b / (tot_t * 1e-6) / 1e9
+    del step_graphs
 
-    sweep = None
-    if args.sweep:
-        sweep = {}
-        for Ms in (1, 2, 4, 8):
-            res = []
-            xq_s = [nv.quantize_act(to_dev(activations_bf16(3, li, Ms, L.K, "outlier")))
-                    for li, L in enumerate(linears)]
-            y_s = [torch.empty((Ms, L.N), dtype=torch.float32, device=dev) for L in linears]
-            for L in linears:
-                ws = nv.workspace(Ms, L.N, L.K)
-            for li, L in enumerate(linears):
-                for r in range(10):
-                    nv.linear(xq_s[li], wsets[r % copies][li], out=y_s[li], ws=ws)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                R = 100
-                e0.record(stream)
-                for r in range(R):
-                    nv.linear(xq_s[li], wsets[r % copies][li], out=y_s[li], ws=ws)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / R * 1e3
-                gbs = gemv_bytes(Ms, L.N, L.K) / (us * 1e-6) / 1e9
-                res.append({"name": L.name, "us": round(us, 3), "GBps": round(gbs, 1)})
-            sweep[f"M{Ms}"] = res
+    # ---- GEMV-only graphs (the roofline kernel), per projection and M
+    def linear_table(lins, sets, Ms, x_src, reps=8):
+        table = {}
+        for Mx in Ms:
+            rows = []
+            for li, L in enumerate(lins):
+                xq = nv.quantize_act(x_src[li][:Mx])
+                y = torch.empty((Mx, L.N), dtype=torch.float32, device=dev)
+                w_ = nv.workspace(Mx, L.N, L.K, dev)
+                n_sets = len(sets)
+
+                def fn(xq=xq, y=y, w_=w_, li=li):
+                    for c in range(n_sets):
+                        nv.linear(xq, sets[c][li], out=y, ws=w_)
+                g = timer.capture(fn)
+                us = timer.time_replays([g], reps) * 1e3 / n_sets
+                xin = torch.empty_like(x_src[li][:Mx]).copy_(x_src[li][:Mx])
+
+                def fq(xin=xin, xq=xq):
+                    for _ in range(16):
+                        nv.quantize_act(xin, out=xq, ws=ws)
+                gq = timer.capture(fq)
+                us_q = timer.time_replays([gq], reps) * 1e3 / 16
+                b = gemv_bytes(Mx, L.N, L.K)
+                rows.append({"name": L.name, "N": L.N, "K": L.K, "us": round(us, 3),
+                             "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                             "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "act_quant_us": round(us_q, 3)})
+                del g, gq
+            table[f"M{Mx}"] = rows
+        return table
+
+    sweep_ms = (M,) if args.no_extras else tuple(sorted({M, 1, 2, 4, 8}))
+    per_linear = linear_table(linears, wsets, sweep_ms, xs)
+    rows = per_linear[f"M{M}"]
+    tot_b = sum(gemv_bytes(M, r["N"], r["K"]) for r in rows)
+    tot_us = sum(r["us"] for r in rows)
+    achieved = tot_b / (tot_us * 1e-6) / 1e9
+    traffic, traffic_note = read_traffic(M)
+    del wsets, base
+
+    out_extra = {}
+    if not args.no_extras:
+        out_extra.update(bench_32b_and_stack(args, torch, nv, dev, timer, linear_table))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -228,23 +334,86 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 x e2m1, e4m3 block-16 scales, fp32 accumulate)",
-        "data": ("synthetic (seeded; bf16 weights 0.02*N(0,1), activations N(0,1) with 1%% x20 "
-                 "outlier channels); weights rotated over %d copies (%.2f GiB)"
-                 % (copies, copies * set_bytes / (1 << 30))),
-        "config": {"workload": f"{wl}_m{M}", "M": M,
+        "dtype": "nvfp4 (e2m1 x e2m1 on fp4 mfma, e4m3 block-16 scales, fp32 accumulate)",
+        "data": ("synthetic (seeded; bf16 weights 0.02*N(0,1), activations N(0,1) with 1% "
+                 f"x20 outlier channels); weights rotated over {copies} copies "
+                 f"({copies * set_bytes / (1 << 30):.2f} GiB)"),
+        "config": {"workload": wl, "M": M,
                    "linears": [f"{L.name} {L.N}x{L.K}" for L in linears],
-                   "path": "per projection: nvfp4_quantize_act + nvfp4_linear (f32 out)"},
+                   "path": "per projection: nvfp4_quantize_act + nvfp4_linear (f32 out), "
+                           "one HIP graph replay per step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "gemv_valu_kernel",
-                     "per_linear": per},
+                     "traffic": traffic, "kernel": GEMV_KERNEL,
+                     "traffic_note": traffic_note,
+                     "launch_us_mean": round(tot_us / len(rows), 3),
+                     "algorithmic_bytes_per_launch": round(tot_b / len(rows))},
+        "per_linear": per_linear,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
-    if sweep is not None:
-        out["sweep_gemv_only"] = sweep
+    out.update(out_extra)
     print(json.dumps(out), flush=True)
+
+
+def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
+    """Qwen3-32B-shaped projections: two seeded layers drawn on the device
+    (torch's Philox generator, 0.02 * N(0,1) bf16), quantized, and copied by
+    device memcpy into args.stack_layers distinct layers; GEMV-only us per
+    projection at M = 1, 4, 8 (rotating over the layers), then the layer
+    stack's decode step replayed args.stack_steps times at M = 1 and 8."""
+    from workloads import QWEN3_32B, activations_bf16
+    lins = QWEN3_32B
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2606_5)
+    seeds = []
+    for _ in range(2):
+        layer = []
+        for L in lins:
+            w = (torch.randn((L.N, L.K), generator=gen, device=dev, dtype=torch.float32)
+                 * 0.02).to(torch.bfloat16)
+            layer.append(nv.quantize_weight(w))
+            del w
+        seeds.append(layer)
+    nl = args.stack_layers
+    layers = [seeds[l] if l < 2 else
+              [nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N, w.K)
+               for w in seeds[l % 2]] for l in range(nl)]
+    torch.cuda.synchronize()
+    wbytes = sum(w.codes.numel() + w.scales.numel() for w in layers[0])
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xs = [to_dev(activations_bf16(4, li, 8, L.K, "student_t")) for li, L in enumerate(lins)]
+    lin32 = linear_table(lins, layers[:max(2, min(nl, int(np.ceil(1.2 * (1 << 30) / wbytes))))],
+                         (1, 4, 8), xs)
+
+    hidden, qkv_n, q_cols, ffn = 5120, 10240, 8192, 25600
+    stack = {"layers": nl, "weight_bytes_per_step": int(nl * wbytes)}
+    for Mx in (1, 8):
+        x_in = to_dev(activations_bf16(5, 0, Mx, hidden, "normal"))
+        y_out = torch.empty((Mx, hidden), dtype=torch.bfloat16, device=dev)
+        st = nv.Stack(Mx, hidden, qkv_n, q_cols, ffn, [tuple(l) for l in layers], x_in, y_out)
+        st.run(5)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st.stream)
+        st.run(args.stack_steps)
+        e1.record(st.stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.stack_steps
+        act = (actq_bytes(Mx, hidden) * 2 + actq_bytes(Mx, q_cols) + actq_bytes(Mx, ffn, 4))
+        outs = Mx * (qkv_n + hidden + 2 * ffn + hidden) * 2
+        lin_act = Mx * (hidden * 2 + q_cols + ffn) * WEIGHT_BYTES_PER_ELEM
+        step_b = nl * (wbytes + act + outs + lin_act)
+        finite = bool(torch.isfinite(y_out.float()).all().item())
+        stack[f"M{Mx}"] = {"us_per_step": round(ms * 1e3, 1),
+                           "GBps": round(step_b / (ms * 1e-3) / 1e9, 1),
+                           "frac": round(step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "replays": args.stack_steps, "output_finite": finite}
+        st.close()
+        del st
+    return {"linears_32b": lin32, "stack_qwen3_32b": stack}
 
 
 if __name__ == "__main__":
