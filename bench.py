@@ -3,8 +3,9 @@
 A step is one pass of the decode hot path over the four projections of a
 Qwen3-8B-shaped decoder layer (QKV 6144x4096, O 4096x4096, gate_up
 24576x4096, down 4096x12288) at M activation rows: for each projection the
-bf16 activation is quantized to NVFP4 on the device (nvfp4_quantize_act)
-and the NVFP4 linear streams the FP4 weights (nvfp4_linear, binary32 out).
+bf16 activation is quantized to NVFP4 and the NVFP4 linear streams the FP4
+weights, in one call (nvfp4_quantize_linear, binary32 out: one kernel whose
+prologue quantizes the activation).
 Weights are quantized once, then copied into enough distinct buffers
 (>= 1.2 GiB) that every step reads weights that are not resident in the
 256 MB Infinity Cache; step i uses copy i mod copies.  Each copy's step is
@@ -14,13 +15,15 @@ synthetic data with the shapes and distributions of that workload.
 
 Prints one JSON line with the step's whole-path algorithmic HBM bytes per
 second (value) and:
-  roofline      the GEMV kernel (gemv_mfma_kernel): algorithmic bytes per
-                launch / its average launch time, from HIP events around
-                replays of GEMV-only graphs on the launch stream; traffic
-                from the committed rocprofv3 counter summary when it was
-                taken on the current kernel source
-  per_linear    GEMV-only us and GB/s per projection at M = 1, 2, 4, 8, and
-                the activation quantizer's us
+  roofline      the step's kernel (gemv_mfma_kernel quantizing its own
+                activation): algorithmic bytes per launch / its average
+                launch time, from HIP events around replays of graphs of
+                that launch alone on the launch stream; traffic from the
+                committed rocprofv3 counter summary when it was taken on the
+                current kernel source
+  per_linear    us and GB/s per projection at M = 1, 2, 4, 8 of the fused
+                call, of the linear alone on a quantized activation, and of
+                the standalone activation quantizer
   linears_32b   the same for the Qwen3-32B-shaped projections at M = 1, 4, 8
   stack         one decode step of a 64-layer stack of the 32B projections
                 (graph replayed 1500 times) at M = 1 and 8
@@ -47,7 +50,8 @@ WEIGHT_BYTES_PER_ELEM = 0.5 + 1.0 / 16
 GEMV_KERNEL = "gemv_mfma_kernel"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_kernel_qwen3_8b_m1_pmc.txt")
 GEMV_SOURCES = ["nvfp4_decode_linear_amd/csrc/gemv_stream.hip",
-                "nvfp4_decode_linear_amd/csrc/gemv_common.hpp"]
+                "nvfp4_decode_linear_amd/csrc/gemv_common.hpp",
+                "nvfp4_decode_linear_amd/csrc/nvfp4_device.hpp"]
 
 
 def gemv_bytes(M, N, K, out_bytes=4):
@@ -61,6 +65,14 @@ def actq_bytes(M, K, in_bytes=2):
     """Algorithmic bytes of an activation quantizer: the input read once,
     codes and scales out (plus the tensor scale)."""
     return M * K * in_bytes + M * K * WEIGHT_BYTES_PER_ELEM + 4
+
+
+def step_linear_bytes(M, N, K, out_bytes=4):
+    """Algorithmic bytes of one projection of the step (quantize + linear):
+    the weight, the bf16 activation read once, its quantized copy written
+    once, the output."""
+    return (N * K * WEIGHT_BYTES_PER_ELEM + 4 + M * K * 2 + M * K * WEIGHT_BYTES_PER_ELEM + 4
+            + M * N * out_bytes)
 
 
 def gemv_source_sha():
@@ -109,7 +121,7 @@ def cpu_baseline(linears, cfg, M, kind, budget_s):
         x = bf16_to_f32(activations_bf16(cfg, li, M, L.K, kind))
         prep.append((x, w_hat, rows, L))
         del wf
-    byts = sum(gemv_bytes(M, rows, L.K) + actq_bytes(M, L.K) for _, _, rows, L in prep)
+    byts = sum(step_linear_bytes(M, rows, L.K) for _, _, rows, L in prep)
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -232,11 +244,11 @@ def main():
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)                             # the calibration copy: 256 MiB read + write
-        xq = [nv.quantize_act(xs[li][:M]) for li in range(len(linears))]
+        xq = [nv.empty_act(M, L.K) for L in linears]
         ys = [torch.empty((M, L.N), dtype=torch.float32, device=dev) for L in linears]
         for c in range(2):
             for li in range(len(linears)):
-                nv.linear(xq[li], wsets[c][li], out=ys[li], ws=ws)
+                nv.quantize_linear(xs[li][:M], wsets[c][li], out=ys[li], xq=xq[li], ws=ws)
         torch.cuda.synchronize()
         return
 
@@ -250,8 +262,7 @@ def main():
     def step_fn(c):
         def fn():
             for li in range(len(linears)):
-                nv.quantize_act(x_m[li], out=xqs[li], ws=ws)
-                nv.linear(xqs[li], wsets[c][li], out=ys[li], ws=ws)
+                nv.quantize_linear(x_m[li], wsets[c][li], out=ys[li], xq=xqs[li], ws=ws)
         return fn
 
     step_graphs = [timer.capture(step_fn(c)) for c in range(copies)]
@@ -270,7 +281,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    step_bytes = sum(gemv_bytes(M, L.N, L.K) + actq_bytes(M, L.K) for L in linears)
+    step_bytes = sum(step_linear_bytes(M, L.N, L.K) for L in linears)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     del step_graphs
 
@@ -292,24 +303,33 @@ def main():
                 us = timer.time_replays([g], reps) * 1e3 / n_sets
                 xin = torch.empty_like(x_src[li][:Mx]).copy_(x_src[li][:Mx])
 
+                def ff(xin=xin, xq=xq, y=y, w_=w_, li=li):
+                    for c in range(n_sets):
+                        nv.quantize_linear(xin, sets[c][li], out=y, xq=xq, ws=w_)
+                gf = timer.capture(ff)
+                us_f = timer.time_replays([gf], reps) * 1e3 / n_sets
+
                 def fq(xin=xin, xq=xq):
                     for _ in range(16):
                         nv.quantize_act(xin, out=xq, ws=ws)
                 gq = timer.capture(fq)
                 us_q = timer.time_replays([gq], reps) * 1e3 / 16
                 b = gemv_bytes(Mx, L.N, L.K)
-                rows.append({"name": L.name, "N": L.N, "K": L.K, "us": round(us, 3),
-                             "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                             "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                bf = step_linear_bytes(Mx, L.N, L.K)
+                rows.append({"name": L.name, "N": L.N, "K": L.K,
+                             "us": round(us_f, 3), "GBps": round(bf / (us_f * 1e-6) / 1e9, 1),
+                             "frac": round(bf / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "linear_only_us": round(us, 3),
+                             "linear_only_GBps": round(b / (us * 1e-6) / 1e9, 1),
                              "act_quant_us": round(us_q, 3)})
-                del g, gq
+                del g, gq, gf
             table[f"M{Mx}"] = rows
         return table
 
     sweep_ms = (M,) if args.no_extras else tuple(sorted({M, 1, 2, 4, 8}))
     per_linear = linear_table(linears, wsets, sweep_ms, xs)
     rows = per_linear[f"M{M}"]
-    tot_b = sum(gemv_bytes(M, r["N"], r["K"]) for r in rows)
+    tot_b = sum(step_linear_bytes(M, r["N"], r["K"]) for r in rows)
     tot_us = sum(r["us"] for r in rows)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
     traffic, traffic_note = read_traffic(M)
@@ -340,8 +360,8 @@ def main():
                  f"({copies * set_bytes / (1 << 30):.2f} GiB)"),
         "config": {"workload": wl, "M": M,
                    "linears": [f"{L.name} {L.N}x{L.K}" for L in linears],
-                   "path": "per projection: nvfp4_quantize_act + nvfp4_linear (f32 out), "
-                           "one HIP graph replay per step"},
+                   "path": "per projection: nvfp4_quantize_linear (activation quantized "
+                           "inside the GEMV, f32 out), one HIP graph replay per step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": GEMV_KERNEL,

@@ -114,7 +114,10 @@ typedef enum {
                                  CU); else at most this many streaming
                                  workgroups, 1..65536 (above 256 several may
                                  share a CU).                               */
-  NVFP4_OPT_COUNT = 8
+  NVFP4_OPT_FUSE_QUANT = 8,   /* 1 (default): nvfp4_quantize_linear quantizes
+                                 the activation inside the GEMV whenever it
+                                 can; 0: always as two launches.           */
+  NVFP4_OPT_COUNT = 9
 } nvfp4_option;
 
 /* ABI version of this header (incremented on any signature change). */
@@ -177,6 +180,25 @@ size_t nvfp4_act_workspace_bytes(int M, int64_t K);
 nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
                                 uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Activation quantization and the decode linear in one call: the result is
+ * bit-identical to nvfp4_quantize_act(x_bf16 -> x_codes, x_scales,
+ * x_gscale) followed by nvfp4_linear on those outputs, which this call also
+ * writes.  When the plan streams the weights on the MFMA kernel and M * K /
+ * 16 <= 1600, a single kernel does both: every workgroup quantizes the
+ * activation in its prologue (reading the bf16 input from L2) and workgroup
+ * 0 writes the quantized copy, so the separate quantizer launch disappears;
+ * otherwise (or with NVFP4_OPT_FUSE_QUANT = 0) the two launches run in
+ * order.  Arguments as for nvfp4_quantize_act and nvfp4_linear; x_codes,
+ * x_scales and x_gscale are outputs here.  The workspace must hold
+ * nvfp4_quantize_linear_workspace_bytes(M, N, K) (the larger of the two
+ * calls' needs; the same memory serves both). */
+size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K);
+nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
+                                   const uint8_t* w_codes, const uint8_t* w_scales,
+                                   const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
+                                   uint8_t* x_scales, float* x_gscale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Fused quantizers of the layer stack (one decode step of a decoder: the
  * end-to-end figure of the "ReSET" GitHub README, captioned under its

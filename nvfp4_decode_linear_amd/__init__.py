@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_WORKSPACE, ERR_HIP = range(6)
 OUT_F32, OUT_BF16 = 0, 1
 OPTIONS = {"gemv_max_m": 0, "split_k": 1, "chunks_per_wave": 2, "nontemporal": 3, "waves": 4,
-           "kernel": 5, "spin_limit": 6, "grid": 7}
+           "kernel": 5, "spin_limit": 6, "grid": 7, "fuse_quant": 8}
 TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
 
 if not os.path.exists(LIB_PATH):
@@ -60,6 +60,10 @@ _linear_workspace_bytes = _sig("nvfp4_linear_workspace_bytes", _c_size, _c_int, 
 _workspace_init = _sig("nvfp4_workspace_init", _c_int, _vp, _c_size, _vp)
 _linear = _sig("nvfp4_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                _c_int, _vp, _c_size, _vp)
+_quantize_linear = _sig("nvfp4_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _c_i64, _vp,
+                        _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp)
+_quantize_linear_workspace_bytes = _sig("nvfp4_quantize_linear_workspace_bytes", _c_size, _c_int,
+                                        _c_i64, _c_i64)
 
 
 class NVFP4Error(RuntimeError):
@@ -326,6 +330,35 @@ def workspace(M: int, N: int, K: int, device="cuda"):
 
 def workspace_init(ws) -> None:
     _check(_workspace_init(_ptr(ws), ws.numel(), _stream(ws)), "nvfp4_workspace_init")
+
+
+def quantize_linear(x, wq: QuantWeight, out_dtype=None, out=None, xq: QuantAct | None = None,
+                    ws=None):
+    """Quantize bf16 x [M][K] and apply the NVFP4 linear in one call (one
+    kernel when possible); returns (y, xq), xq the quantized activation."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    if K != wq.K:
+        raise ValueError("K mismatch")
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    y = out if out is not None else torch.empty((M, wq.N), dtype=out_dtype, device=x.device)
+    q = xq if xq is not None else empty_act(M, K, x.device)
+    if ws is None:
+        need = _quantize_linear_workspace_bytes(M, wq.N, K)
+        ws = workspace(M, wq.N, K, x.device)
+        if ws.numel() < need:
+            raise NVFP4Error(ERR_WORKSPACE, "quantize_linear workspace")
+    _check(_quantize_linear(M, wq.N, K, _ptr(x), x.stride(0), _ptr(wq.codes), _ptr(wq.scales),
+                            _ptr(wq.gscale), _ptr(y), od, _ptr(q.codes), _ptr(q.scales),
+                            _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(y)),
+           "nvfp4_quantize_linear")
+    return y, q
 
 
 def linear(xq: QuantAct, wq: QuantWeight, out_dtype=None, out=None, ws=None):

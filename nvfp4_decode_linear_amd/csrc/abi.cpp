@@ -23,7 +23,7 @@ constexpr int kLayoutVersion = 1;
 constexpr int kMaxM = 8;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}};
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}, {1}};
 thread_local int t_last_hip = 0;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -81,6 +81,7 @@ bool split_ok(int M, int cpw, int waves) {
 }
 
 constexpr int64_t kLdsBudget = 160 * 1024;
+constexpr int64_t kFuseMaxBlocks = 1600;
 
 void finish_workspace(GemvPlan& p, int M) {
   // The arrival counters live in a fixed region at the start of the
@@ -240,6 +241,9 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
     case NVFP4_OPT_GRID:
       if (value < 0 || value > 65536) return NVFP4_ERR_INVALID_ARG;
       break;
+    case NVFP4_OPT_FUSE_QUANT:
+      if (value != 0 && value != 1) return NVFP4_ERR_INVALID_ARG;
+      break;
     default: return NVFP4_ERR_UNSUPPORTED;
   }
   g_opts[opt].store(value);
@@ -312,6 +316,55 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
   const hipError_t e = nvfp4::launch_quantize_act(
       x_bf16, M, (int)K, ldx, x_codes, x_scales, x_gscale, static_cast<uint32_t*>(workspace),
       (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(), (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K) {
+  const size_t lin = nvfp4_linear_workspace_bytes(M, N, K);
+  const size_t act = nvfp4_act_workspace_bytes(M, K);
+  return lin > act ? lin : act;
+}
+
+nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
+                                   const uint8_t* w_codes, const uint8_t* w_scales,
+                                   const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
+                                   uint8_t* x_scales, float* x_gscale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (M < 1 || !valid_nk(N, K) || N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
+      (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks || ldx < K || ldx % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!x_bf16 || !w_codes || !w_scales || !w_gscale || !y || !x_codes || !x_scales || !x_gscale)
+    return NVFP4_ERR_INVALID_ARG;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
+      !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
+      !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
+    return NVFP4_ERR_INVALID_ARG;
+  const GemvPlan p = make_plan(M, N, K);
+  // Every workgroup quantizes the whole activation in its prologue: worth it
+  // up to ~1600 blocks (measured: M * K / 16 = 2048 runs slower fused than
+  // as two launches).
+  const int64_t blocks = (int64_t)M * (K >> 4);
+  const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
+                     blocks <= nvfp4::qa_max_blocks(p.waves) && blocks <= kFuseMaxBlocks;
+  if (!fused) {
+    // two launches: the activation quantizer, then the linear on its output
+    if (nvfp4_status st = nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale,
+                                             workspace, workspace_bytes, stream);
+        st != NVFP4_OK)
+      return st;
+    return nvfp4_linear(M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y,
+                        out_dtype, workspace, workspace_bytes, stream);
+  }
+  if (p.ws_bytes > 0) {
+    if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < p.ws_bytes) return NVFP4_ERR_WORKSPACE;
+  }
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_gemv_stream(
+      p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y, out_dtype,
+      workspace, (hipStream_t)stream, x_bf16, ldx, x_codes, x_scales, x_gscale);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 

@@ -38,6 +38,13 @@ struct GemvArgs {
   int tiles;
   int batch;     // streaming kernels: items reduced together (LDS slots)
   int waves;     // streaming kernels: wavefronts per workgroup
+  // activation quantized inside the GEMV (nvfp4_quantize_linear): the bf16
+  // input [M][ldx] and the canonical NVFP4 outputs workgroup 0 writes
+  const uint16_t* xb;
+  int64_t ldx;
+  uint8_t* oc;
+  uint8_t* os;
+  float* og;
 };
 
 __device__ inline u32x4 load_codes(const uint8_t* p, bool nt) {

@@ -35,6 +35,7 @@ using namespace gemv;
 
 constexpr int kStreamXpt = 4;   // activation blocks per thread in the first batch
 constexpr int kStreamXrest = 8; // ... and in each later batch (large M * K)
+constexpr int kQaBpt = 4;       // bf16 blocks per thread when the GEMV quantizes
 
 // Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
 // activation row, 8 (<= 256 VGPRs) for two or three rows, whose register
@@ -125,7 +126,7 @@ __device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g
 // compile-time constants on every path (the paths never merge), so the
 // compiler's memory wait counts stay exact: where paths with different
 // numbers of outstanding loads merge, it waits for all of them.
-template <int M, int RG, int XS, bool MF, bool SPLIT>
+template <int M, int RG, int XS, bool MF, bool SPLIT, bool QA>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const int NW = a.waves;                     // = blockDim.x / 64 (not read from the
                                               // dispatch packet: that load would
@@ -199,42 +200,84 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
   };
 
-  // ---- 2. activation into LDS, after the first weight loads are issued
-  // (so no weight load waits behind it): a first batch of blocks per thread
-  // loaded together (out-of-range blocks read block 0 and are zeroed, so no
-  // load is conditional), any rest (large M * K only) after it.
-  auto prologue = [&]() __attribute__((always_inline)) {
-    u32x2 xc[kStreamXpt];
-    uint32_t xs[kStreamXpt];
+  // ---- 2. activation into LDS: the first batch of blocks per thread (loaded
+  // before the weights, see below), any rest (large M * K only) loaded now.
+  // Binary32 product of the two tensor scales (with QA set by the prologue,
+  // which runs before the first item is finished).
+  float g = QA ? 0.0f : __fmul_rn(a.xg[0], a.wg[0]);
+  uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
+  u32x2 xc0[QA ? 1 : kStreamXpt];             // else: its first quantized activation blocks
+  uint32_t xs0[QA ? 1 : kStreamXpt];
+  auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
+    if constexpr (MF) {
+      xlds[(m * kc * 4 + kb) * 2] = c.x;
+      xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
+      sa[kb * M + m] = (_Float16)e4m3_to_f32(sc);
+    } else {
+      decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
+    }
+  };
+  // QA: the activation quantizer inside the prologue.  Every workgroup reads
+  // the whole bf16 activation (at most kQaBpt blocks per thread, all loads in
+  // flight together), takes the exact tensor maximum (bf16 magnitudes as
+  // integers: workgroup, then wave, then LDS), and quantizes every block with
+  // the quantizer's own arithmetic straight into its LDS staging; workgroup 0
+  // also writes the canonical codes, scales and tensor scale, bit-identical
+  // to the standalone activation quantizer's.
+  // (the bf16 loads are issued before the first weight loads, so waiting for
+  // them does not wait for the weights)
+  auto quantize_prologue = [&]() __attribute__((always_inline)) {
+    const int T = 64 * NW;
+    const int nreal = M * kb_row;
+    auto& v = qv;
+    uint32_t amax = 0;
 #pragma unroll
-    for (int r = 0; r < kStreamXpt; ++r) {
-      const int i = threadIdx.x + r * 64 * NW;
-      const int m = i / (kc * 4), kb = i - m * (kc * 4);
-      const bool ok = i < nblk && kb < kb_row;
-      const int64_t cofs = ok ? (int64_t)m * (a.K >> 1) + 8 * kb : 0;
-      const int64_t sofs = ok ? (int64_t)m * kb_row + kb : 0;
-      xc[r] = *reinterpret_cast<const u32x2*>(a.xc + cofs);
-      xs[r] = a.xs[sofs];
-      if (!ok) {
-        xc[r] = u32x2{0u, 0u};
-        xs[r] = 0u;
+    for (int r = 0; r < kQaBpt; ++r) {      // branch free: exact wait counts
+      const uint32_t b = absmax_bits(v[r]);
+      amax = max(amax, (int)threadIdx.x + r * T < nreal ? b : 0u);
+    }
+    amax = wave_max_u32(amax);
+    uint32_t* wmax = reinterpret_cast<uint32_t*>(red);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = 0;
+    for (int w = 0; w < NW; ++w) amax = max(amax, wmax[w]);
+    const float sg = tensor_scale(bf16_to_f32(amax));
+    g = __fmul_rn(sg, a.wg[0]);
+    const bool out = blockIdx.x == 0;
+#pragma unroll
+    for (int r = 0; r < kQaBpt; ++r) {
+      const int i = (int)threadIdx.x + r * T;
+      if (i < nreal) {
+        const int m = i / kb_row, kb = i - m * kb_row;
+        const BlockQ q = quantize_block_bf16(v[r], sg);
+        put(m, kb, u32x2{q.lo, q.hi}, q.scale);
+        if (out) {
+          *reinterpret_cast<u32x2*>(a.oc + (int64_t)m * (a.K >> 1) + 8 * kb) = u32x2{q.lo, q.hi};
+          a.os[(int64_t)m * kb_row + kb] = (uint8_t)q.scale;
+        }
       }
     }
-    auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
-      if constexpr (MF) {
-        xlds[(m * kc * 4 + kb) * 2] = c.x;
-        xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
-        sa[kb * M + m] = (_Float16)e4m3_to_f32(sc);
-      } else {
-        decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
-      }
-    };
+    if (out && threadIdx.x == 0) *a.og = sg;
+    const int npad = kc * 4 - kb_row;                 // zero blocks up to the padded K
+    for (int i = threadIdx.x; i < M * npad; i += T) {
+      const int m = i / npad;
+      put(m, kb_row + (i - m * npad), u32x2{0u, 0u}, 0u);
+    }
+    __syncthreads();
+  };
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (QA) {
+      quantize_prologue();
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < kStreamXpt; ++r) {
       const int i = threadIdx.x + r * 64 * NW;
       if (i < nblk) {
         const int m = i / (kc * 4), kb = i - m * (kc * 4);
-        put(m, kb, xc[r], xs[r]);
+        const bool ok = kb < kb_row;
+        put(m, kb, ok ? xc0[r] : u32x2{0u, 0u}, ok ? xs0[r] : 0u);
       }
     }
     // the rest in batches of kStreamXrest blocks per thread, all loads of a
@@ -264,7 +307,6 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     __syncthreads();
   };
 
-  const float g = __fmul_rn(a.xg[0], a.wg[0]);
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
@@ -279,7 +321,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // the stream), then a barrier before the slots are reused.
   int ci = blockIdx.x, jb = 0, done = 0, batch_first = blockIdx.x;
   Item cit = item(ci);
-  auto flush = [&]() __attribute__((always_inline)) {
+  auto flush = [&](bool last) __attribute__((always_inline)) {
     __syncthreads();
     for (int i = threadIdx.x; i < jb * M * 32; i += 64 * NW) {
       const int j = i / (M * 32), mn = i - j * (M * 32);
@@ -295,7 +337,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         if (n < a.N) store_y(a, m, n, v * g);
       }
     }
-    __syncthreads();
+    if (!last) __syncthreads();               // the slots are reused by the next batch
     jb = 0;
   };
   auto finish_tile = [&]() __attribute__((always_inline)) {
@@ -311,7 +353,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     ci += G;
     cit = item(ci);
     if (jb == a.batch || done == nitem) {
-      flush();
+      flush(done == nitem);
       batch_first = ci;
     }
   };
@@ -408,6 +450,27 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   };
 
   static_assert(A >= 2 && A <= 4 && SL <= 5, "ring of 2 to 5 slots");
+  // The activation loads go out before the first weight loads, so waiting
+  // for them does not wait for the weights (addresses clamped into range,
+  // out-of-range blocks zeroed at use: no load is conditional).
+  if constexpr (QA) {
+    const int T = 64 * NW;
+    const int nreal = M * kb_row;
+#pragma unroll
+    for (int r = 0; r < kQaBpt; ++r) {
+      const int i = min((int)threadIdx.x + r * T, nreal - 1);
+      const int m = i / kb_row, kb = i - m * kb_row;
+      load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kStreamXpt; ++r) {
+      const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
+      const int m = i / (kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
+      xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
+      xs0[r] = a.xs[(int64_t)m * kb_row + kb];
+    }
+  }
   if (ng >= A) {
     static_for<A>([&](auto T) __attribute__((always_inline)) { refill(T); });
     prologue();
@@ -436,30 +499,30 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 template <int M, bool SPLIT>
 __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, stream_ring_groups(M), 0, false, SPLIT>(a, lds);
+  stream_body<M, stream_ring_groups(M), 0, false, SPLIT, false>(a, lds);
 }
 
-template <int M, bool SPLIT>
+template <int M, bool SPLIT, bool QA>
 __global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT>(a, lds);
+  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA>(a, lds);
 }
 
-template <int M, bool MF, bool SPLIT>
+template <int M, bool MF, bool SPLIT, bool QA>
 hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch);
   const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
   const void* fn;
   if constexpr (MF)
-    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT>);
+    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA>);
   else
     fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M, SPLIT>);
   static hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   if constexpr (MF)
-    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT>), dim3((unsigned)p.grid), dim3(64 * p.waves),
-                       lds, s, a);
+    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA>), dim3((unsigned)p.grid),
+                       dim3(64 * p.waves), lds, s, a);
   else
     hipLaunchKernelGGL((gemv_stream_kernel<M, SPLIT>), dim3((unsigned)p.grid),
                        dim3(64 * p.waves), lds, s, a);
@@ -470,7 +533,15 @@ template <int M, bool MF>
 hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
     return hipErrorInvalidValue;
-  return p.splits > 1 ? launch_ms<M, MF, true>(p, a, s) : launch_ms<M, MF, false>(p, a, s);
+  if constexpr (MF) {
+    if (a.xb) {
+      if (M * (a.K >> 4) > kQaBpt * 64 * p.waves) return hipErrorInvalidValue;
+      return p.splits > 1 ? launch_ms<M, true, true, true>(p, a, s)
+                          : launch_ms<M, true, false, true>(p, a, s);
+    }
+  }
+  return p.splits > 1 ? launch_ms<M, MF, true, false>(p, a, s)
+                      : launch_ms<M, MF, false, false>(p, a, s);
 }
 
 }  // namespace
@@ -478,8 +549,14 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, const uint8_t* xc,
                               const uint8_t* xs, const float* xg, const uint8_t* wc,
                               const uint8_t* ws, const float* wg, void* y, int out_bf16,
-                              void* workspace, hipStream_t s) {
+                              void* workspace, hipStream_t s, const uint16_t* xb, int64_t ldx,
+                              uint8_t* oc, uint8_t* os, float* og) {
   GemvArgs a = {};
+  a.xb = xb;
+  a.ldx = ldx;
+  a.oc = oc;
+  a.os = os;
+  a.og = og;
   a.xc = xc;
   a.xs = xs;
   a.xg = xg;

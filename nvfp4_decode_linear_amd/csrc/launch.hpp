@@ -86,6 +86,13 @@ hipError_t launch_gemv_split(const GemvPlan& p, int M, int64_t N, int64_t K,
 hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               const uint8_t* xc, const uint8_t* xs, const float* xg,
                               const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,
-                              int out_bf16, void* workspace, hipStream_t s);
+                              int out_bf16, void* workspace, hipStream_t s,
+                              const uint16_t* xb = nullptr, int64_t ldx = 0,
+                              uint8_t* oc = nullptr, uint8_t* os = nullptr,
+                              float* og = nullptr);
+
+// Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
+// (4 bf16 blocks per thread).
+inline int64_t qa_max_blocks(int waves) { return (int64_t)4 * 64 * waves; }
 
 }  // namespace nvfp4

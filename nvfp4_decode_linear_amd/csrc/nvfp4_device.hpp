@@ -59,6 +59,27 @@ __device__ inline uint32_t f32_to_e2m1_rne_sat(float y) {
   return c | ((__float_as_uint(y) >> 28) & 8u);
 }
 
+// One block of 16 bf16 values (32 bytes, 16-byte aligned) as 8 packed pairs.
+__device__ inline void load_block_bf16(const uint16_t* p, uint32_t (&v)[8]) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 8);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Largest |x| of a bf16 block as a bf16 magnitude pattern (these order like
+// integers, so the maximum is exact).
+__device__ inline uint32_t absmax_bits(const uint32_t (&v)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = v[i] & 0x7FFF7FFFu;
+    m = max(m, max(a & 0xFFFFu, a >> 16));
+  }
+  return m;
+}
+
 // Tensor scale from the tensor amax: amax / 2688, replaced by 1 when 0.
 __device__ inline float tensor_scale(float amax) {
   float sg = __fdiv_rn(amax, kAmaxToScale);

@@ -17,23 +17,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline void load_block_bf16(const uint16_t* p, uint32_t (&v)[8]) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 8);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-__device__ inline uint32_t absmax_bits(const uint32_t (&v)[8]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a = v[i] & 0x7FFF7FFFu;
-    m = max(m, max(a & 0xFFFFu, a >> 16));
-  }
-  return m;
-}
-
 // ------------------------------------------------------------ activations
 //
 // The tensor amax is a reduction over every element of the M x K activation

@@ -77,10 +77,11 @@ nvfp4_status enqueue_step(nvfp4_stack* s, void* st) {
                                         s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) != NVFP4_OK)
       break;
     if ((r = lin(w[kQkv], c.qkv_n, c.hidden, s->qkv)) != NVFP4_OK) break;
-    if ((r = nvfp4_quantize_act(s->qkv, M, c.q_cols, c.qkv_n, s->a_codes, s->a_scales,
-                                s->a_gscale, s->ws, s->ws_bytes, st)) != NVFP4_OK)
+    // quantize the q columns and apply O (one kernel when it fits)
+    if ((r = nvfp4_quantize_linear(M, c.hidden, c.q_cols, s->qkv, c.qkv_n, w[kO].codes,
+                                   w[kO].scales, w[kO].gscale, s->o, NVFP4_OUT_BF16, s->a_codes,
+                                   s->a_scales, s->a_gscale, s->ws, s->ws_bytes, st)) != NVFP4_OK)
       break;
-    if ((r = lin(w[kO], c.hidden, c.q_cols, s->o)) != NVFP4_OK) break;
     if ((r = nvfp4_rmsnorm_quantize_act(s->o, M, c.hidden, c.hidden, c.eps, s->a_codes,
                                         s->a_scales, s->a_gscale, nullptr, s->ws, s->ws_bytes,
                                         st)) != NVFP4_OK)
@@ -132,7 +133,7 @@ nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weigh
   const int64_t kmax = std::max({c.hidden, c.q_cols, c.ffn});
   size_t ws = 256;
   ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.qkv_n, c.hidden));
-  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.q_cols));
+  ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, c.hidden, c.q_cols));
   ws = std::max(ws, nvfp4_linear_workspace_bytes(M, 2 * c.ffn, c.hidden));
   ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.ffn));
   s->ws_bytes = ws;

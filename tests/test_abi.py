@@ -236,3 +236,23 @@ def test_fused_quantize_argument_errors(lib, no_gpu):
              None) == 1                                                             # h_out
     assert s(FAKE, 1, 512, 1000, FAKE, FAKE, FAKE, None, None, 0, None) == 1        # ld < 2K
     assert s(FAKE, 1, 512, 1024, FAKE, FAKE, FAKE, None, None, 0, None) == 3        # no device
+
+
+def test_quantize_linear_argument_errors(lib, no_gpu):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.nvfp4_quantize_linear
+    f.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                  ctypes.c_size_t, vp]
+    ok = (FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert f(9, 256, 512, FAKE, 512, *ok) == 2
+    assert f(1, 256, 520, FAKE, 520, *ok) == 1                 # K % 16
+    assert f(1, 256, 512, FAKE, 500, *ok) == 1                 # ldx < K
+    assert f(1, 256, 512, ctypes.c_void_p(0x1008), 512, *ok) == 1   # x alignment
+    bad = list(ok)
+    bad[5] = None
+    assert f(1, 256, 512, FAKE, 512, *bad) == 1                # x_codes output required
+    assert f(1, 256, 512, FAKE, 512, *ok) == 3                 # no device
+    lib.nvfp4_quantize_linear_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
+    lib.nvfp4_quantize_linear_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.nvfp4_quantize_linear_workspace_bytes(8, 24576, 4096) == 16   # act sync record
+    assert lib.nvfp4_quantize_linear_workspace_bytes(1, 24576, 4096) == 0

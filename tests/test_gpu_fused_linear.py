@@ -1,0 +1,105 @@
+"""nvfp4_quantize_linear: the activation quantizer inside the GEMV's
+prologue.  Its output and the quantized activation it writes must be
+bit-identical to the two-launch path (nvfp4_quantize_act, then nvfp4_linear)
+and the quantized activation bit-exact to the oracle; shapes past the fused
+kernel's limit take the two launches."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import note, to_dev_bf16
+from workloads import QWEN3_8B, QWEN3_32B, activations_bf16, bf16_to_f32, weights_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    import nvfp4_decode_linear_amd as nv
+    return nv
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _same(a, b):
+    return np.array_equal(a.cpu().contiguous().view(-1).view(__import__("torch").uint8).numpy(),
+                          b.cpu().contiguous().view(-1).view(__import__("torch").uint8).numpy())
+
+
+def _both(nv, x, wq, out_dtype):
+    y1, q1 = nv.quantize_linear(x, wq, out_dtype=out_dtype)
+    _sync()
+    nv.set_option("fuse_quant", 0)
+    try:
+        y0, q0 = nv.quantize_linear(x, wq, out_dtype=out_dtype)
+        _sync()
+    finally:
+        nv.set_option("fuse_quant", 1)
+    return (y1, q1), (y0, q0)
+
+
+SHAPES = [(256, 512, 1), (6144, 4096, 1), (4096, 4096, 2), (24576, 4096, 4), (4096, 12288, 1),
+          (4096, 4096, 8), (100, 1040, 3), (33, 16, 8), (5120, 25600, 1), (10240, 5120, 8)]
+
+
+@pytest.mark.parametrize("N,K,M", SHAPES)
+def test_fused_matches_two_launches_and_oracle(nv, N, K, M):
+    import torch
+    note(f"quantize_linear N={N} K={K} M={M}")
+    w16 = weights_bf16(8, N % 7, N, K)
+    x16 = activations_bf16(8, K % 5, M, K, "outlier")
+    wq = nv.quantize_weight(to_dev_bf16(w16))
+    x = to_dev_bf16(x16)
+    for od in (torch.float32, torch.bfloat16):
+        (y1, q1), (y0, q0) = _both(nv, x, wq, od)
+        assert _same(y1, y0), f"output differs from the two-launch path ({od})"
+        for a, b in ((q1.codes, q0.codes), (q1.scales, q0.scales), (q1.gscale, q0.gscale)):
+            assert _same(a, b)
+    ref = oracle.quantize(bf16_to_f32(x16))
+    assert np.array_equal(q1.codes.cpu().numpy(), ref.codes)
+    assert np.array_equal(q1.scales.cpu().numpy(), ref.scales)
+    assert q1.gscale.cpu().numpy().view(np.uint32)[0] == np.asarray(ref.gscale,
+                                                                    np.float32).view(np.uint32)
+
+
+def test_fused_strided_input_and_graph_replay(nv):
+    import torch
+    L = QWEN3_8B[0]
+    M = 2
+    note(f"quantize_linear strided + graph replay N={L.N} K={L.K} M={M}")
+    w16 = weights_bf16(8, 1, L.N, L.K)
+    wq = nv.quantize_weight(to_dev_bf16(w16))
+    wide = torch.empty((M, L.K + 64), dtype=torch.bfloat16, device="cuda")
+    x = wide[:, :L.K]
+    y = torch.empty((M, L.N), dtype=torch.float32, device="cuda")
+    q = nv.empty_act(M, L.K)
+    ws = nv.workspace(M, L.N, L.K)
+    wide.copy_(to_dev_bf16(activations_bf16(8, 2, M, L.K + 64, "outlier")))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.quantize_linear(x, wq, out=y, xq=q, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        nv.quantize_linear(x, wq, out=y, xq=q, ws=ws)
+    for r in range(3):
+        x16 = activations_bf16(8, 10 + r, M, L.K + 64, "student_t")
+        wide.copy_(to_dev_bf16(x16))
+        torch.empty(1 << 20, device="cuda").fill_(3.0)
+        _sync()
+        g.replay()
+        _sync()
+        xq = nv.quantize_act(wide[:, :L.K])
+        y0 = nv.linear(xq, wq)
+        _sync()
+        assert _same(y, y0), f"replay {r}"
+        assert _same(q.codes, xq.codes) and _same(q.scales, xq.scales)
