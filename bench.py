@@ -49,9 +49,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 WEIGHT_BYTES_PER_ELEM = 0.5 + 1.0 / 16
 GEMV_KERNEL = "gemv_mfma_kernel"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_mfma_kernel_qwen3_8b_m1_pmc.txt")
-GEMV_SOURCES = ["nvfp4_decode_linear_amd/csrc/gemv_stream.hip",
-                "nvfp4_decode_linear_amd/csrc/gemv_common.hpp",
-                "nvfp4_decode_linear_amd/csrc/nvfp4_device.hpp"]
+GEMV_SOURCES = (["nvfp4_decode_linear_amd/csrc/gemv_stream.hpp",
+                 "nvfp4_decode_linear_amd/csrc/gemv_stream.hip",
+                 "nvfp4_decode_linear_amd/csrc/gemv_common.hpp",
+                 "nvfp4_decode_linear_amd/csrc/nvfp4_device.hpp"]
+                + [f"nvfp4_decode_linear_amd/csrc/gemv_stream_m{m}.hip" for m in range(1, 9)])
 
 
 def gemv_bytes(M, N, K, out_bytes=4):

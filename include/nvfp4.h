@@ -117,7 +117,12 @@ typedef enum {
   NVFP4_OPT_FUSE_QUANT = 8,   /* 1 (default): nvfp4_quantize_linear quantizes
                                  the activation inside the GEMV whenever it
                                  can; 0: always as two launches.           */
-  NVFP4_OPT_COUNT = 9
+  NVFP4_OPT_HALF_TILES = 9,   /* MFMA streaming kernel on 16-row half tiles
+                                 (16x16x128 MFMA, twice the work items): 0
+                                 (default) = when 32-row tiles fill at most
+                                 half the 256 workgroups, 1 = never, 2 =
+                                 always (one K slice only).                */
+  NVFP4_OPT_COUNT = 10
 } nvfp4_option;
 
 /* ABI version of this header (incremented on any signature change). */

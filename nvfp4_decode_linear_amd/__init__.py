@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_WORKSPACE, ERR_HIP = range(6)
 OUT_F32, OUT_BF16 = 0, 1
 OPTIONS = {"gemv_max_m": 0, "split_k": 1, "chunks_per_wave": 2, "nontemporal": 3, "waves": 4,
-           "kernel": 5, "spin_limit": 6, "grid": 7, "fuse_quant": 8}
+           "kernel": 5, "spin_limit": 6, "grid": 7, "fuse_quant": 8, "half_tiles": 9}
 TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
 
 if not os.path.exists(LIB_PATH):

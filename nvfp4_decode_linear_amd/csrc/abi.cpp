@@ -23,7 +23,7 @@ constexpr int kLayoutVersion = 1;
 constexpr int kMaxM = 8;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}, {1}};
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}, {1}, {0}};
 thread_local int t_last_hip = 0;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -136,18 +136,24 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     const int max_waves = want_mfma ? 8 : (M == 1 ? 16 : 8);  // as compiled
     const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves)
                                      : std::min(max_waves, 8);
-    const int s0 = force_split > 0 ? (int)force_split : stream_splits(p.tiles, p.kc);
+    // 16-row half tiles (MFMA only, one K slice): twice the work items, for
+    // shapes whose 32-row tiles leave CUs idle.
+    const int64_t force_half = g_opts[NVFP4_OPT_HALF_TILES].load();
+    const bool h16 = want_mfma && force_split <= 1 &&
+                     (force_half == 2 || (force_half == 0 && 2 * p.tiles <= kStreamGrid));
+    const int gc = h16 ? 8 : 4;                              // chunks per ring group
+    const int s0 = h16 ? 1 : force_split > 0 ? (int)force_split : stream_splits(p.tiles, p.kc);
     const int kcs = (p.kc + s0 - 1) / s0;                 // chunks per slice
-    const int cpw = (int)round_up((kcs + want - 1) / want, 4);
+    const int cpw = (int)round_up((kcs + want - 1) / want, gc);
     const int waves = (kcs + cpw - 1) / cpw;
     const int cps = cpw * waves;
     const int splits = (p.kc + cps - 1) / cps;
-    const int64_t items = (int64_t)p.tiles * splits;
+    const int64_t items = (int64_t)p.tiles * (h16 ? 2 : 1) * splits;
     const int64_t force_grid = g_opts[NVFP4_OPT_GRID].load();
     const int grid = (int)std::min<int64_t>(items, force_grid > 0 ? force_grid : kStreamGrid);
     const int64_t per_wg = (items + grid - 1) / grid;
     const int64_t act = (int64_t)nvfp4::stream_act_lds(M, p.kc, want_mfma);
-    const int64_t slot = (int64_t)waves * M * 32 * 4;
+    const int64_t slot = (int64_t)waves * M * (h16 ? 16 : 32) * 4;
     const int64_t batch = std::min<int64_t>(per_wg, (kLdsBudget - act) / slot);
     if (waves <= max_waves && batch >= 1 &&
         (splits == 1 || per_wg <= batch * waves * M * 32)) {
@@ -158,6 +164,7 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
       p.cps = cps;
       p.splits = splits;
       p.batch = (int)batch;
+      p.h16 = h16 ? 1 : 0;
       p.grid = grid;        // <= 256: one resident workgroup per CU (the launch reserves LDS)
       finish_workspace(p, M);
       return p;
@@ -243,6 +250,9 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
       break;
     case NVFP4_OPT_FUSE_QUANT:
       if (value != 0 && value != 1) return NVFP4_ERR_INVALID_ARG;
+      break;
+    case NVFP4_OPT_HALF_TILES:
+      if (value < 0 || value > 2) return NVFP4_ERR_INVALID_ARG;
       break;
     default: return NVFP4_ERR_UNSUPPORTED;
   }

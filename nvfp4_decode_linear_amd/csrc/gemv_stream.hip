@@ -1,550 +1,8 @@
-// Persistent streaming GEMV for the small-M NVFP4 W4A4 decode linear
-// (gfx950): the default kernels whenever the whole K extent of the
-// activation fits in LDS.
-//
-// The operation is the one of "ReSET" GitHub README, "Core components",
-// item 2 (nvfp4r): for M <= 8 rows the FP4 weights are streamed once and
-// every loaded weight serves all M rows.  On gfx950:
-//
-//  * one workgroup of up to 16 wavefronts per CU walks work items blockIdx.x,
-//    blockIdx.x + gridDim.x, ...; an item is a 32-row tile and a K slice
-//    (normally all of K), whose 4-record groups go to the waves round robin;
-//  * every wave keeps 3 groups of 4 weight records (1 KiB each, one 64-lane
-//    load) plus their scale record in flight and refills a group as soon as
-//    it has consumed it; the wave's groups of consecutive items form one
-//    stream, so the next item's loads are in flight while this one finishes;
-//  * the dot: either on FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-//    E8M0 scales on a block-diagonal activation operand, giving exact
-//    per-16-block partial dot products that the VALU scales by both E4M3
-//    block scales), or on the VALU (the activation decoded once into LDS as
-//    f16 x~ = e2m1(code) * e4m3(scale), exact, then v_dot2 per block);
-//  * an item's partial sums are left per wave in LDS and summed in fixed
-//    wave order (the same result on every run) once per batch of items, then
-//    scaled by both tensor scales and written as binary32 or bf16; with
-//    several K slices they go through the workspace instead, and the last
-//    slice of a tile to arrive sums the slices in slice order.
-#include <type_traits>
-
-#include "gemv_common.hpp"
+// Dispatch of the persistent streaming GEMV kernels (gemv_stream.hpp) to the
+// per-row-count translation units gemv_stream_m<M>.hip.
+#include "gemv_stream.hpp"
 
 namespace nvfp4 {
-
-namespace {
-
-using namespace gemv;
-
-constexpr int kStreamXpt = 4;   // activation blocks per thread in the first batch
-constexpr int kStreamXrest = 8; // ... and in each later batch (large M * K)
-constexpr int kQaBpt = 4;       // bf16 blocks per thread when the GEMV quantizes
-
-// Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
-// activation row, 8 (<= 256 VGPRs) for two or three rows, whose register
-// footprint does not fit 128 without spilling.  Four or more rows use the
-// split kernel (the streaming one would spill).
-constexpr int kStreamMaxM = 3;
-constexpr int stream_max_waves(int M) { return M == 1 ? 16 : 8; }
-
-// Groups of 4 weight records (4 KiB) each wave keeps in flight.
-constexpr int stream_ring_groups(int M) { return M == 3 ? 2 : 3; }
-
-// The MFMA variant keeps 16 result registers per chunk but decodes nothing;
-// its ring has a spare slot (3 groups in flight while it computes, 4 for
-// four or more rows, whose longer epilogue needs the longer lookahead), which
-// needs the 256-register budget of 8 waves.
-constexpr int mfma_max_waves(int) { return 8; }
-constexpr int mfma_ring_groups(int M) { return M >= 4 ? 4 : 3; }
-
-// The grid holds at most one workgroup per CU.  The hardware dispatcher
-// packs workgroups onto a CU while its registers and LDS last, so every
-// workgroup reserves more than half of the CU's 160 KiB LDS: then no CU can
-// hold two and the min(tiles, 256) workgroups spread over distinct CUs.
-constexpr size_t kStreamLdsReserve = 80 * 1024 + 1024;
-
-template <int V>
-using ic = std::integral_constant<int, V>;
-
-// f(ic<0>), f(ic<1>), ..., f(ic<N - 1>), unrolled at compile time
-template <int I, int N>
-struct StaticFor {
-  template <class F>
-  __device__ __forceinline__ static void run(F&& f) {
-    if constexpr (I < N) {
-      f(ic<I>{});
-      StaticFor<I + 1, N>::run(f);
-    }
-  }
-};
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  StaticFor<0, N>::run(f);
-}
-
-// Split-K tail of the streaming kernels, after the workgroup's last item:
-// wait until its partial sums are stored, count each of its items in at its
-// row tile's arrival counter (thread j takes item j, so the atomics overlap),
-// and for every tile where this workgroup arrived last, sum the slices in
-// slice order (the result does not depend on arrival order), scale, store,
-// and put the counter back to zero for the next call.  At most batch * NW *
-// M * 32 items per workgroup (the flags reuse the reduction slots).
-template <int M>
-__device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g, float* red) {
-  const int S = a.splits, G = gridDim.x;
-  uint32_t* flag = reinterpret_cast<uint32_t*>(red);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  const int nt = 64 * a.waves;
-  for (int j = threadIdx.x; j < nitem; j += nt) {
-    const int tile = ((int)blockIdx.x + j * G) / S;
-    const uint32_t old =
-        __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    flag[j] = old == (uint32_t)(S - 1);
-  }
-  __syncthreads();
-  // every (item, row, column) of the items this workgroup completes at once
-  for (int i = threadIdx.x; i < nitem * M * 32; i += nt) {
-    const int j = i / (M * 32), mn = i - j * (M * 32);
-    if (!flag[j]) continue;
-    const int m = mn >> 5, n = mn & 31;
-    const int n0 = ((int)blockIdx.x + j * G) / S * kTileN;
-    const float* pp = a.part + (int64_t)m * a.n_pad + n0 + n;
-    const int64_t st = (int64_t)M * a.n_pad;
-    float v = 0.0f;
-    for (int t = 0; t < S; ++t)
-      v += __hip_atomic_load(pp + t * st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n0 + n < a.N) store_y(a, m, n0 + n, v * g);
-  }
-  for (int j = threadIdx.x; j < nitem; j += nt) {
-    if (flag[j]) {
-      const int tile = ((int)blockIdx.x + j * G) / S;
-      __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// One workgroup's whole job.  Every wave keeps RG groups of 4 weight records
-// in flight.  The numbers of groups the stream starts with and ends with are
-// compile-time constants on every path (the paths never merge), so the
-// compiler's memory wait counts stay exact: where paths with different
-// numbers of outstanding loads merge, it waits for all of them.
-template <int M, int RG, int XS, bool MF, bool SPLIT, bool QA>
-__device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
-  const int NW = a.waves;                     // = blockDim.x / 64 (not read from the
-                                              // dispatch packet: that load would
-                                              // delay every other one)
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5;
-  const bool nt = a.nontemporal != 0;
-  const int kc = a.kc;
-  const int row_dw = kc * 32;
-  // VALU: x~ as f16 pairs [M][kc * 32 dwords].  MFMA: raw activation codes
-  // [M][kc * 4 blocks][2 dwords], then the E4M3 activation scales as f16
-  // (every E4M3 value is an f16 value) [kc * 4 blocks][M], padded to a
-  // dword.  Either is followed by the reduction slots [batch][NW][M][32]
-  // floats.
-  uint32_t* xlds = lds;
-  _Float16* sa = reinterpret_cast<_Float16*>(lds + M * kc * 8);
-  float* red = reinterpret_cast<float*>(MF ? lds + M * kc * 8 + (kc * 4 * M + 1) / 2
-                                           : lds + M * row_dw);
-  const int kb_row = a.K >> 4;
-  const int nblk = M * kc * 4;                // activation 16-blocks, padded K
-  const int cpw = a.cpw;                      // chunks per wave per item, multiple of 4
-
-  const int S = SPLIT ? a.splits : 1;         // K slices per row tile
-  const int G = gridDim.x;
-  const int nitem = (a.tiles * S - (int)blockIdx.x + G - 1) / G;
-  const int ng = nitem * (cpw >> 2);          // groups of 4 records in this wave's stream
-  // Work item i = (row tile i / S, K slice i % S).  The slice's chunks go
-  // to the waves in groups of 4 (one scale record), round robin: this wave
-  // owns chunks cb + NW * 4j + k (j < cpw / 4, k < 4, cb = slice * cps + 4 *
-  // wave), so at any time the workgroup's waves read adjacent records.  A
-  // group past K (last slice only) re-reads the tile's last group, with its
-  // scales zeroed.
-  struct Item {
-    int tile, slice, cb;
-  };
-  auto item = [&](int i) __attribute__((always_inline)) {
-    Item it;
-    if constexpr (SPLIT) {
-      it.tile = i / S;
-      it.slice = i - it.tile * S;
-    } else {
-      it.tile = i;
-      it.slice = 0;
-    }
-    it.cb = it.slice * a.cps + 4 * wave;
-    return it;
-  };
-
-  // ---- 1. this wave's records form one stream: its cpw chunks of the
-  // workgroup's first item, then of its second item, ...
-  const uint8_t* wbase = a.wc + 16 * lane;
-  const uint8_t* sbase = a.ws + 8 * lane;
-  int li = blockIdx.x, loff = 0;              // load cursor: item, chunk offset
-  Item lit = item(li);
-  u32x4 ring[RG + XS][4];
-  u32x2 rsc[RG + XS];
-  auto refill = [&](auto Q) __attribute__((always_inline)) {
-    constexpr int q = decltype(Q)::value;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t r = (int64_t)lit.tile * kc + min(lit.cb + loff * NW + k, kc - 4 + k);
-      if (k == 0) rsc[q] = load_scales(sbase + (r >> 2) * kScaleRecord, nt);
-      ring[q][k] = load_codes(wbase + r * kCodeRecord, nt);
-    }
-    loff += 4;
-    if (loff == cpw) {
-      loff = 0;
-      li += G;
-      lit = item(li);
-    }
-  };
-
-  // ---- 2. activation into LDS: the first batch of blocks per thread (loaded
-  // before the weights, see below), any rest (large M * K only) loaded now.
-  // Binary32 product of the two tensor scales (with QA set by the prologue,
-  // which runs before the first item is finished).
-  float g = QA ? 0.0f : __fmul_rn(a.xg[0], a.wg[0]);
-  uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
-  u32x2 xc0[QA ? 1 : kStreamXpt];             // else: its first quantized activation blocks
-  uint32_t xs0[QA ? 1 : kStreamXpt];
-  auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
-    if constexpr (MF) {
-      xlds[(m * kc * 4 + kb) * 2] = c.x;
-      xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
-      sa[kb * M + m] = (_Float16)e4m3_to_f32(sc);
-    } else {
-      decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
-    }
-  };
-  // QA: the activation quantizer inside the prologue.  Every workgroup reads
-  // the whole bf16 activation (at most kQaBpt blocks per thread, all loads in
-  // flight together), takes the exact tensor maximum (bf16 magnitudes as
-  // integers: workgroup, then wave, then LDS), and quantizes every block with
-  // the quantizer's own arithmetic straight into its LDS staging; workgroup 0
-  // also writes the canonical codes, scales and tensor scale, bit-identical
-  // to the standalone activation quantizer's.
-  // (the bf16 loads are issued before the first weight loads, so waiting for
-  // them does not wait for the weights)
-  auto quantize_prologue = [&]() __attribute__((always_inline)) {
-    const int T = 64 * NW;
-    const int nreal = M * kb_row;
-    auto& v = qv;
-    uint32_t amax = 0;
-#pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {      // branch free: exact wait counts
-      const uint32_t b = absmax_bits(v[r]);
-      amax = max(amax, (int)threadIdx.x + r * T < nreal ? b : 0u);
-    }
-    amax = wave_max_u32(amax);
-    uint32_t* wmax = reinterpret_cast<uint32_t*>(red);
-    if (lane == 0) wmax[wave] = amax;
-    __syncthreads();
-    amax = 0;
-    for (int w = 0; w < NW; ++w) amax = max(amax, wmax[w]);
-    const float sg = tensor_scale(bf16_to_f32(amax));
-    g = __fmul_rn(sg, a.wg[0]);
-    const bool out = blockIdx.x == 0;
-#pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {
-      const int i = (int)threadIdx.x + r * T;
-      if (i < nreal) {
-        const int m = i / kb_row, kb = i - m * kb_row;
-        const BlockQ q = quantize_block_bf16(v[r], sg);
-        put(m, kb, u32x2{q.lo, q.hi}, q.scale);
-        if (out) {
-          *reinterpret_cast<u32x2*>(a.oc + (int64_t)m * (a.K >> 1) + 8 * kb) = u32x2{q.lo, q.hi};
-          a.os[(int64_t)m * kb_row + kb] = (uint8_t)q.scale;
-        }
-      }
-    }
-    if (out && threadIdx.x == 0) *a.og = sg;
-    const int npad = kc * 4 - kb_row;                 // zero blocks up to the padded K
-    for (int i = threadIdx.x; i < M * npad; i += T) {
-      const int m = i / npad;
-      put(m, kb_row + (i - m * npad), u32x2{0u, 0u}, 0u);
-    }
-    __syncthreads();
-  };
-  auto prologue = [&]() __attribute__((always_inline)) {
-    if constexpr (QA) {
-      quantize_prologue();
-      return;
-    }
-#pragma unroll
-    for (int r = 0; r < kStreamXpt; ++r) {
-      const int i = threadIdx.x + r * 64 * NW;
-      if (i < nblk) {
-        const int m = i / (kc * 4), kb = i - m * (kc * 4);
-        const bool ok = kb < kb_row;
-        put(m, kb, ok ? xc0[r] : u32x2{0u, 0u}, ok ? xs0[r] : 0u);
-      }
-    }
-    // the rest in batches of kStreamXrest blocks per thread, all loads of a
-    // batch in flight together
-    for (int base = threadIdx.x + kStreamXpt * 64 * NW; base < nblk;
-         base += kStreamXrest * 64 * NW) {
-      u32x2 c[kStreamXrest];
-      uint32_t sc[kStreamXrest];
-#pragma unroll
-      for (int r = 0; r < kStreamXrest; ++r) {
-        const int i = min(base + r * 64 * NW, nblk - 1);
-        const int m = i / (kc * 4), kb = i - m * (kc * 4);
-        const int kbc = min(kb, kb_row - 1);
-        c[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kbc);
-        sc[r] = a.xs[(int64_t)m * kb_row + kbc];
-      }
-#pragma unroll
-      for (int r = 0; r < kStreamXrest; ++r) {
-        const int i = base + r * 64 * NW;
-        if (i < nblk) {
-          const int m = i / (kc * 4), kb = i - m * (kc * 4);
-          const bool ok = kb < kb_row;
-          put(m, kb, ok ? c[r] : u32x2{0u, 0u}, ok ? sc[r] : 0u);
-        }
-      }
-    }
-    __syncthreads();
-  };
-
-  float acc[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-
-  // Item-boundary reduction.  The K halves meet at once (lanes l, l ^ 32);
-  // each wave then leaves its partial sum of the item in its own LDS slot
-  // [item in batch][wave][M][32] and streams on without waiting for the
-  // other waves.  After `batch` items (normally all of the workgroup's), one
-  // barrier, then the waves' partials are summed in fixed wave order (the
-  // result is the same on every run) and stored: as the output with one K
-  // slice, else as the slice's partial sum (device-coherent, combined after
-  // the stream), then a barrier before the slots are reused.
-  int ci = blockIdx.x, jb = 0, done = 0, batch_first = blockIdx.x;
-  Item cit = item(ci);
-  auto flush = [&](bool last) __attribute__((always_inline)) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < jb * M * 32; i += 64 * NW) {
-      const int j = i / (M * 32), mn = i - j * (M * 32);
-      const float* sl = red + j * (NW * M * 32) + mn;
-      float v = sl[0];
-      for (int q = 1; q < NW; ++q) v += sl[q * M * 32];
-      const Item it = item(batch_first + j * G);
-      const int m = mn >> 5, n = it.tile * kTileN + (mn & 31);
-      if constexpr (SPLIT) {
-        __hip_atomic_store(a.part + ((int64_t)it.slice * M + m) * a.n_pad + n, v,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        if (n < a.N) store_y(a, m, n, v * g);
-      }
-    }
-    if (!last) __syncthreads();               // the slots are reused by the next batch
-    jb = 0;
-  };
-  auto finish_tile = [&]() __attribute__((always_inline)) {
-    float* sl = red + jb * (NW * M * 32) + wave * (M * 32);
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      acc[m] += __shfl_xor(acc[m], 32, 64);
-      if (h == 0) sl[m * 32 + lane] = acc[m];
-      acc[m] = 0.0f;
-    }
-    ++jb;
-    ++done;
-    ci += G;
-    cit = item(ci);
-    if (jb == a.batch || done == nitem) {
-      flush(done == nitem);
-      batch_first = ci;
-    }
-  };
-
-  // Consume ring group q: chunks cb + NW * coff + 0..3 of the current item.
-  // Branch free (wait counts stay exact): a chunk past K reads a valid
-  // activation chunk and gets a zero block scale, so it adds exactly 0.
-  // MFMA A operand: lane l holds row r = l % 32 of the 32 x 64 block-diagonal
-  // activation tile, K half l / 32.  Row r is activation row ma, block ja of
-  // the chunk, chosen so that the 32 x 32 result lands with every lane
-  // holding its own weight row n = l % 32 and its own two blocks 2h, 2h + 1
-  // (result v = 4i + q of lane l is tile row 8i + 4h + q = (m 2i + q / 2,
-  // block 2h + q % 2)).  The lane's 16 A bytes are the block's 8 code bytes,
-  // in the low or high half, or zero when the block lies in the other K half
-  // (or the row is past M).
-  const int ra = lane & 31;
-  const int ma = 2 * (ra >> 3) + ((ra & 3) >> 1);
-  const int ja = 2 * ((ra >> 2) & 1) + (ra & 1);
-  const bool a_on = (h == ((ra >> 2) & 1)) && (ma < M);
-  const bool a_lo = a_on && (ra & 1) == 0, a_hi = a_on && (ra & 1) != 0;
-  const uint32_t* xa_row = xlds + (ma < M ? ma : 0) * kc * 8 + ja * 2;
-
-  int coff = 0;
-  auto consume = [&](auto Q) __attribute__((always_inline)) {
-    constexpr int q = decltype(Q)::value;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = cit.cb + coff * NW + k;
-      uint32_t sb = (k < 2 ? rsc[q].x : rsc[q].y) >> (16 * (k & 1));
-      sb = c < kc ? sb : 0u;
-      const int cx = min(c, kc - 1);
-      if constexpr (MF) {
-        const uint32_t* xp = xa_row + cx * 8;
-        const uint32_t a0 = xp[0], a1 = xp[1];
-        const v8i A = {(int)(a_lo ? a0 : 0u), (int)(a_lo ? a1 : 0u), (int)(a_hi ? a0 : 0u),
-                       (int)(a_hi ? a1 : 0u), 0, 0, 0, 0};
-        const u32x4 wv = ring[q][k];
-        const v8i B = {(int)wv.x, (int)wv.y, (int)wv.z, (int)wv.w, 0, 0, 0, 0};
-        const v16f C = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, v16f{}, 4, 4, 0, 127,
-                                                                       0, 127);
-        const float sw0 = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
-        const float sw1 = __builtin_amdgcn_cvt_f32_fp8(sb, 1);
-        const _Float16* sap = sa + (4 * cx + 2 * h) * M;       // [block 2h + b][m]
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = 2 * (v >> 2) + ((v & 3) >> 1), b = v & 1;
-          if constexpr (true) {
-            if (m < M) acc[m] = fmaf(C[v], (float)sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
-          }
-        }
-      } else {
-        dot_chunk<M>(ring[q][k], sb, xlds + ((cx * 64 + 32 * h) >> 1), row_dw, acc);
-      }
-    }
-    coff += 4;
-    if (coff == cpw) {
-      finish_tile();
-      coff = 0;
-    }
-  };
-
-  // The stream.  Group g of the wave's stream lives in slot g % SL; A = RG
-  // groups are loaded ahead.  With a spare slot (SL = A + 1) each step first
-  // issues the load of the group A ahead into the slot consumed by the
-  // previous step, then consumes its own group, so A groups stay in flight
-  // while the wave computes; without one (SL = A) it consumes, then reuses
-  // the slot.  The numbers of groups loaded and consumed on every path are
-  // compile-time constants, so the memory wait counts stay exact.
-  constexpr int A = RG, SL = RG + XS;
-  auto step = [&](auto T) __attribute__((always_inline)) {    // position t of SL
-    constexpr int t = decltype(T)::value;
-    if constexpr (SL > A) {
-      refill(ic<(t + A) % SL>{});
-      consume(ic<t % SL>{});
-    } else {
-      consume(ic<t % SL>{});
-      refill(ic<t % SL>{});
-    }
-  };
-  // last A + x groups, x of them still to load
-  auto tail = [&](auto X) __attribute__((always_inline)) {
-    constexpr int x = decltype(X)::value;
-    static_for<A + x>([&](auto T) __attribute__((always_inline)) {
-      constexpr int t = decltype(T)::value;
-      if constexpr (t < x) step(ic<t>{}); else consume(ic<t % SL>{});
-    });
-  };
-  // fewer than A groups in all: load them, then consume them
-  auto short_stream = [&](auto NG) __attribute__((always_inline)) {
-    constexpr int n = decltype(NG)::value;
-    static_for<n>([&](auto T) __attribute__((always_inline)) { refill(T); });
-    prologue();
-    static_for<n>([&](auto T) __attribute__((always_inline)) { consume(T); });
-  };
-
-  static_assert(A >= 2 && A <= 4 && SL <= 5, "ring of 2 to 5 slots");
-  // The activation loads go out before the first weight loads, so waiting
-  // for them does not wait for the weights (addresses clamped into range,
-  // out-of-range blocks zeroed at use: no load is conditional).
-  if constexpr (QA) {
-    const int T = 64 * NW;
-    const int nreal = M * kb_row;
-#pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {
-      const int i = min((int)threadIdx.x + r * T, nreal - 1);
-      const int m = i / kb_row, kb = i - m * kb_row;
-      load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < kStreamXpt; ++r) {
-      const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
-      const int m = i / (kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
-      xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
-      xs0[r] = a.xs[(int64_t)m * kb_row + kb];
-    }
-  }
-  if (ng >= A) {
-    static_for<A>([&](auto T) __attribute__((always_inline)) { refill(T); });
-    prologue();
-    int gi = 0;
-    for (; gi + SL + A <= ng; gi += SL) static_for<SL>(step);
-    switch (ng - gi - A) {                    // 0 .. SL - 1 groups still to load
-      case 0: tail(ic<0>{}); break;
-      case 1: tail(ic<1>{}); break;
-      case 2: if constexpr (SL > 2) tail(ic<(SL > 2 ? 2 : 0)>{}); break;
-      case 3: if constexpr (SL > 3) tail(ic<(SL > 3 ? 3 : 0)>{}); break;
-      default: if constexpr (SL > 4) tail(ic<(SL > 4 ? 4 : 0)>{}); break;
-    }
-  } else {
-    switch (ng) {                             // 1 .. A - 1
-      case 1: short_stream(ic<1>{}); break;
-      case 2: if constexpr (A > 2) short_stream(ic<(A > 2 ? 2 : 1)>{}); break;
-      default: if constexpr (A > 3) short_stream(ic<(A > 3 ? 3 : 1)>{}); break;
-    }
-  }
-  if constexpr (SPLIT) split_tail<M>(a, nitem, g, red);
-}
-
-// Launch: blockDim.x = 64 * a.waves (at most stream_max_waves(M) or
-// mfma_max_waves(M)); dynamic LDS = the activation followed by the
-// reduction slots (stream_lds_need), at least kStreamLdsReserve.
-template <int M, bool SPLIT>
-__global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(GemvArgs a) {
-  extern __shared__ uint32_t lds[];
-  stream_body<M, stream_ring_groups(M), 0, false, SPLIT, false>(a, lds);
-}
-
-template <int M, bool SPLIT, bool QA>
-__global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
-  extern __shared__ uint32_t lds[];
-  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA>(a, lds);
-}
-
-template <int M, bool MF, bool SPLIT, bool QA>
-hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch);
-  const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
-  const void* fn;
-  if constexpr (MF)
-    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA>);
-  else
-    fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M, SPLIT>);
-  static hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  if constexpr (MF)
-    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA>), dim3((unsigned)p.grid),
-                       dim3(64 * p.waves), lds, s, a);
-  else
-    hipLaunchKernelGGL((gemv_stream_kernel<M, SPLIT>), dim3((unsigned)p.grid),
-                       dim3(64 * p.waves), lds, s, a);
-  return hipGetLastError();
-}
-
-template <int M, bool MF>
-hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
-    return hipErrorInvalidValue;
-  if constexpr (MF) {
-    if (a.xb) {
-      if (M * (a.K >> 4) > kQaBpt * 64 * p.waves) return hipErrorInvalidValue;
-      return p.splits > 1 ? launch_ms<M, true, true, true>(p, a, s)
-                          : launch_ms<M, true, false, true>(p, a, s);
-    }
-  }
-  return p.splits > 1 ? launch_ms<M, MF, true, false>(p, a, s)
-                      : launch_ms<M, MF, false, false>(p, a, s);
-}
-
-}  // namespace
 
 hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, const uint8_t* xc,
                               const uint8_t* xs, const float* xg, const uint8_t* wc,
@@ -581,24 +39,17 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
   a.out_bf16 = out_bf16;
   a.nontemporal = p.nontemporal;
   a.tiles = p.tiles;
-  if (p.kind == kGemvMfma) {
-    switch (M) {
-      case 1: return launch_m<1, true>(p, a, s);
-      case 2: return launch_m<2, true>(p, a, s);
-      case 3: return launch_m<3, true>(p, a, s);
-      case 4: return launch_m<4, true>(p, a, s);
-      case 5: return launch_m<5, true>(p, a, s);
-      case 6: return launch_m<6, true>(p, a, s);
-      case 7: return launch_m<7, true>(p, a, s);
-      case 8: return launch_m<8, true>(p, a, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  static_assert(kStreamMaxM == 3, "one case per supported row count");
+  const bool mf = p.kind == kGemvMfma;
+  if (!mf && M > 3) return hipErrorInvalidValue;          // the VALU dot: M <= 3
   switch (M) {
-    case 1: return launch_m<1, false>(p, a, s);
-    case 2: return launch_m<2, false>(p, a, s);
-    case 3: return launch_m<3, false>(p, a, s);
+    case 1: return launch_stream_rows<1>(p, a, s, mf);
+    case 2: return launch_stream_rows<2>(p, a, s, mf);
+    case 3: return launch_stream_rows<3>(p, a, s, mf);
+    case 4: return launch_stream_rows<4>(p, a, s, mf);
+    case 5: return launch_stream_rows<5>(p, a, s, mf);
+    case 6: return launch_stream_rows<6>(p, a, s, mf);
+    case 7: return launch_stream_rows<7>(p, a, s, mf);
+    case 8: return launch_stream_rows<8>(p, a, s, mf);
     default: return hipErrorInvalidValue;
   }
 }

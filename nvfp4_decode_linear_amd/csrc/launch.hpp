@@ -24,8 +24,8 @@ inline size_t stream_act_lds(int M, int kc, bool mfma) {
   return mfma ? (size_t)M * kc * 32 + ((size_t)kc * 4 * M + 1) / 2 * 4
               : (size_t)M * kc * 128;
 }
-inline size_t stream_lds_need(int M, int kc, int waves, bool mfma, int batch) {
-  return stream_act_lds(M, kc, mfma) + (size_t)batch * waves * M * 32 * 4;
+inline size_t stream_lds_need(int M, int kc, int waves, bool mfma, int batch, int rows = 32) {
+  return stream_act_lds(M, kc, mfma) + (size_t)batch * waves * M * rows * 4;
 }
 
 struct GemvPlan {
@@ -39,6 +39,7 @@ struct GemvPlan {
   int cps;       // chunks per K slice (= cpw * waves)
   int splits;    // K slices per row tile (1 = no split-K tail, no workspace)
   int batch;     // streaming kernels: items whose partial sums share one barrier
+  int h16;       // MFMA streaming kernel on 16-row half tiles (16x16x128 MFMA)
   int depth;     // weight records in flight per wavefront (stream kernel)
   int grid;      // workgroups launched
   int nontemporal;

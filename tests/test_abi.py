@@ -80,6 +80,7 @@ def test_options_roundtrip_and_validation(lib):
     assert lib.nvfp4_set_option(6, 1) == 0
     assert lib.nvfp4_get_option(6, ctypes.byref(v)) == 0 and v.value == 1
     assert lib.nvfp4_set_option(6, 0) == 0
+    assert lib.nvfp4_set_option(9, 3) == 1          # half tiles: 0, 1 or 2
     assert lib.nvfp4_set_option(2, 6) == 1          # chunks per wave must be a multiple of 4
     assert lib.nvfp4_set_option(3, 2) == 1
     assert lib.nvfp4_set_option(99, 0) == 2
@@ -90,12 +91,18 @@ def test_workspace_bytes(lib):
     assert lib.nvfp4_linear_workspace_bytes(9, 4096, 4096) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 4096, 24) == 0
     # The streaming kernel (the default whenever the activation fits in LDS)
-    # needs no workspace unless it splits K, which it does only for fewer
-    # than 64 row tiles: N = 1024 (32 tiles) and K = 4096 split into 8
-    # slices: counters plus [8][M][N] partial sums.
+    # needs no workspace unless it splits K.  With at most 128 row tiles it
+    # runs on 16-row half tiles, never split; on 32-row tiles it splits only
+    # below 64 tiles: N = 1024 (32 tiles), K = 4096 in 8 slices, counters
+    # plus [8][M][N] partial sums.
     assert lib.nvfp4_linear_workspace_bytes(1, 24576, 4096) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 4096, 4096) == 0
-    assert lib.nvfp4_linear_workspace_bytes(1, 1024, 4096) == 64 * 1024 + 8 * 1024 * 4
+    assert lib.nvfp4_linear_workspace_bytes(1, 1024, 4096) == 0
+    assert lib.nvfp4_set_option(9, 1) == 0
+    try:
+        assert lib.nvfp4_linear_workspace_bytes(1, 1024, 4096) == 64 * 1024 + 8 * 1024 * 4
+    finally:
+        assert lib.nvfp4_set_option(9, 0) == 0
     assert lib.nvfp4_linear_workspace_bytes(8, 5120, 25600) == 0     # codes + f16 scales fit
     assert lib.nvfp4_linear_workspace_bytes(8, 5120, 40960) > 0      # too big for LDS: split-K
     # Forcing the split-K kernel on the 8B down projection (128 tiles) needs

@@ -49,8 +49,15 @@ SHAPES = [(256, 512, 1), (6144, 4096, 1), (4096, 4096, 2), (24576, 4096, 4), (40
           (4096, 4096, 8), (100, 1040, 3), (33, 16, 8), (5120, 25600, 1), (10240, 5120, 8)]
 
 
+@pytest.fixture(params=[0, 1, 2], ids=["tiles_auto", "full_tiles", "half_tiles"])
+def half_tiles(nv, request):
+    nv.set_option("half_tiles", request.param)
+    yield request.param
+    nv.set_option("half_tiles", 0)
+
+
 @pytest.mark.parametrize("N,K,M", SHAPES)
-def test_fused_matches_two_launches_and_oracle(nv, N, K, M):
+def test_fused_matches_two_launches_and_oracle(nv, half_tiles, N, K, M):
     import torch
     note(f"quantize_linear N={N} K={K} M={M}")
     w16 = weights_bf16(8, N % 7, N, K)

@@ -62,24 +62,28 @@ UNIT_SHAPES = [(256, 512), (4096, 4096), (24576, 4096), (4096, 12288), (5120, 81
                (100, 1040), (33, 16), (64, 25600)]
 
 
-KERNELS = {  # name: (kernel option, split_k option)
-    "auto": (0, 0), "valu_stream": (1, 0), "split": (2, 0), "mfma": (3, 1), "mfma_split3": (3, 3),
+KERNELS = {  # name: (kernel option, split_k option, half_tiles option)
+    "auto": (0, 0, 0), "valu_stream": (1, 0, 0), "split": (2, 0, 0), "mfma": (3, 1, 1),
+    "mfma_split3": (3, 3, 1), "mfma_h16": (3, 0, 2),
 }
 
 
 @pytest.fixture
 def kernel(nv, request):
-    """Force one GEMV kernel (and K slice count) for the test; "auto" is the
-    library's own choice."""
-    k, sp = KERNELS[request.param]
+    """Force one GEMV kernel (K slice count, tile height) for the test;
+    "auto" is the library's own choice."""
+    k, sp, hh = KERNELS[request.param]
     nv.set_option("kernel", k)
     nv.set_option("split_k", sp)
+    nv.set_option("half_tiles", hh)
     yield request.param
     nv.set_option("kernel", 0)
     nv.set_option("split_k", 0)
+    nv.set_option("half_tiles", 0)
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3", "mfma_h16"],
+                         indirect=True)
 @pytest.mark.parametrize("N,K", UNIT_SHAPES)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
 def test_unit_scale_bit_exact(nv, kernel, M, N, K):
@@ -95,7 +99,8 @@ def test_unit_scale_bit_exact(nv, kernel, M, N, K):
                              f"{got[bad[0][0], bad[1][0]]} vs {ref[bad[0][0], bad[1][0]]}"
 
 
-@pytest.mark.parametrize("kernel", ["auto", "valu_stream", "split", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "valu_stream", "split", "mfma", "mfma_h16"],
+                         indirect=True)
 @pytest.mark.parametrize("M", [1, 3, 4, 8])
 def test_power_of_two_scales_bit_exact(nv, kernel, M):
     """Block scales 2^-2 .. 2^2 keep every partial sum a small dyadic
@@ -160,7 +165,7 @@ def test_tiny_full(nv):
     _check_sampled(nv, y, w16, x16, wq, np.arange(L.N))
 
 
-@pytest.mark.parametrize("kernel", ["auto", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "mfma", "mfma_h16"], indirect=True)
 @pytest.mark.parametrize("lin", range(4))
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_8b_shapes_sampled(nv, kernel, lin, M):
@@ -172,7 +177,7 @@ def test_8b_shapes_sampled(nv, kernel, lin, M):
     _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(lin)))
 
 
-@pytest.mark.parametrize("kernel", ["auto", "mfma"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "mfma", "mfma_h16"], indirect=True)
 @pytest.mark.parametrize("lin", range(4))
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_32b_shapes_sampled(nv, kernel, lin, M):
@@ -195,7 +200,8 @@ def test_bf16_output(nv, M):
     _check_sampled(nv, y, w16, x16, wq, _cols(L.N, np.random.default_rng(5)), out_bf16=True)
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3", "mfma_h16"],
+                         indirect=True)
 @pytest.mark.parametrize("N,K,M", [(1, 16, 1), (33, 16, 8), (100, 1040, 3), (4097, 784, 5),
                                    (31, 25600, 7), (300, 8000, 2)])
 def test_ragged_and_degenerate(nv, kernel, N, K, M):
@@ -220,7 +226,8 @@ def test_zero_activation_gives_zero(nv):
     assert torch.count_nonzero(y).item() == 0
 
 
-@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3"], indirect=True)
+@pytest.mark.parametrize("kernel", ["auto", "split", "mfma", "mfma_split3", "mfma_h16"],
+                         indirect=True)
 def test_run_to_run_bit_stable(nv, kernel):
     L = QWEN3_8B[3]
     note(f"linear determinism kernel={kernel} M=8 N={L.N} K={L.K}")
