@@ -205,6 +205,24 @@ nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* 
                                    uint8_t* x_scales, float* x_gscale, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* The unweighted per-row RMS norm, the activation quantizer and the linear
+ * in one call: y = linear(Q(h)) with h as for nvfp4_rmsnorm_quantize_act
+ * (x_codes, x_scales, x_gscale and, if not NULL, h_out [M][K] binary32 are
+ * written).  In one kernel when nvfp4_quantize_linear would fuse; its
+ * workgroups then sum each row's squares in their own fixed order (the same
+ * in every workgroup and on every run, but not the standalone quantizer's,
+ * so h may differ from nvfp4_rmsnorm_quantize_act's in the last bits; either
+ * way the codes are exactly Q of the h that is written).  Otherwise
+ * nvfp4_rmsnorm_quantize_act then nvfp4_linear.  K <= 32768; workspace as for
+ * nvfp4_quantize_linear. */
+nvfp4_status nvfp4_rmsnorm_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16,
+                                           int64_t ldx, float eps, const uint8_t* w_codes,
+                                           const uint8_t* w_scales, const float* w_gscale,
+                                           void* y, int out_dtype, uint8_t* x_codes,
+                                           uint8_t* x_scales, float* x_gscale, float* h_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
 /* Fused quantizers of the layer stack (one decode step of a decoder: the
  * end-to-end figure of the "ReSET" GitHub README, captioned under its
  * introduction, runs the NVFP4 linears of whole layers; the stack between

@@ -64,6 +64,9 @@ _quantize_linear = _sig("nvfp4_quantize_linear", _c_int, _c_int, _c_i64, _c_i64,
                         _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp)
 _quantize_linear_workspace_bytes = _sig("nvfp4_quantize_linear_workspace_bytes", _c_size, _c_int,
                                         _c_i64, _c_i64)
+_rmsnorm_quantize_linear = _sig("nvfp4_rmsnorm_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp,
+                                _c_i64, ctypes.c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
+                                _vp, _vp, _c_size, _vp)
 
 
 class NVFP4Error(RuntimeError):
@@ -358,6 +361,32 @@ def quantize_linear(x, wq: QuantWeight, out_dtype=None, out=None, xq: QuantAct |
                             _ptr(wq.gscale), _ptr(y), od, _ptr(q.codes), _ptr(q.scales),
                             _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(y)),
            "nvfp4_quantize_linear")
+    return y, q
+
+
+def rmsnorm_quantize_linear(x, wq: QuantWeight, eps=1e-6, out_dtype=None, out=None,
+                            xq: QuantAct | None = None, h_out=None, ws=None):
+    """Unweighted per-row RMS norm of bf16 x [M][K], quantization and the
+    NVFP4 linear in one call (one kernel when possible); returns (y, xq)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    if K != wq.K:
+        raise ValueError("K mismatch")
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    y = out if out is not None else torch.empty((M, wq.N), dtype=out_dtype, device=x.device)
+    q = xq if xq is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(M, wq.N, K, x.device)
+    _check(_rmsnorm_quantize_linear(M, wq.N, K, _ptr(x), x.stride(0), float(eps), _ptr(wq.codes),
+                                    _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), od, _ptr(q.codes),
+                                    _ptr(q.scales), _ptr(q.gscale), _nullable(h_out), _ptr(ws),
+                                    ws.numel(), _stream(y)), "nvfp4_rmsnorm_quantize_linear")
     return y, q
 
 

@@ -335,21 +335,27 @@ size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K) {
   return lin > act ? lin : act;
 }
 
-nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
-                                   const uint8_t* w_codes, const uint8_t* w_scales,
-                                   const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
-                                   uint8_t* x_scales, float* x_gscale, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+namespace {
+
+// nvfp4_quantize_linear (rms = 0) and nvfp4_rmsnorm_quantize_linear (rms = 1)
+nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, int M, int64_t N, int64_t K,
+                                  const uint16_t* x_bf16, int64_t ldx, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, const float* w_gscale, void* y,
+                                  int out_dtype, uint8_t* x_codes, uint8_t* x_scales,
+                                  float* x_gscale, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
   if (M < 1 || !valid_nk(N, K) || N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
       (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks || ldx < K || ldx % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rms && (K > nvfp4::kPrepMaxK || !(eps >= 0.0f) || !std::isfinite(eps)))
     return NVFP4_ERR_INVALID_ARG;
   if (!x_bf16 || !w_codes || !w_scales || !w_gscale || !y || !x_codes || !x_scales || !x_gscale)
     return NVFP4_ERR_INVALID_ARG;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
       !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
-      !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
+      !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2) || (h_out && !aligned(h_out, 16)))
     return NVFP4_ERR_INVALID_ARG;
   const GemvPlan p = make_plan(M, N, K);
   // Every workgroup quantizes the whole activation in its prologue: worth it
@@ -359,11 +365,13 @@ nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* 
   const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
                      blocks <= nvfp4::qa_max_blocks(p.waves) && blocks <= kFuseMaxBlocks;
   if (!fused) {
-    // two launches: the activation quantizer, then the linear on its output
-    if (nvfp4_status st = nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale,
-                                             workspace, workspace_bytes, stream);
-        st != NVFP4_OK)
-      return st;
+    // two launches: the (RMS norm +) activation quantizer, then the linear
+    const nvfp4_status st =
+        rms ? nvfp4_rmsnorm_quantize_act(x_bf16, M, K, ldx, eps, x_codes, x_scales, x_gscale,
+                                         h_out, workspace, workspace_bytes, stream)
+            : nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale, workspace,
+                                 workspace_bytes, stream);
+    if (st != NVFP4_OK) return st;
     return nvfp4_linear(M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y,
                         out_dtype, workspace, workspace_bytes, stream);
   }
@@ -374,8 +382,32 @@ nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* 
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
   const hipError_t e = nvfp4::launch_gemv_stream(
       p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y, out_dtype,
-      workspace, (hipStream_t)stream, x_bf16, ldx, x_codes, x_scales, x_gscale);
+      workspace, (hipStream_t)stream, x_bf16, ldx, x_codes, x_scales, x_gscale, rms, eps, h_out);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
+                                   const uint8_t* w_codes, const uint8_t* w_scales,
+                                   const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
+                                   uint8_t* x_scales, float* x_gscale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return quantize_linear_impl(0, 0.0f, nullptr, M, N, K, x_bf16, ldx, w_codes, w_scales, w_gscale,
+                              y, out_dtype, x_codes, x_scales, x_gscale, workspace,
+                              workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_rmsnorm_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16,
+                                           int64_t ldx, float eps, const uint8_t* w_codes,
+                                           const uint8_t* w_scales, const float* w_gscale,
+                                           void* y, int out_dtype, uint8_t* x_codes,
+                                           uint8_t* x_scales, float* x_gscale, float* h_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  return quantize_linear_impl(1, eps, h_out, M, N, K, x_bf16, ldx, w_codes, w_scales, w_gscale, y,
+                              out_dtype, x_codes, x_scales, x_gscale, workspace, workspace_bytes,
+                              stream);
 }
 
 namespace {

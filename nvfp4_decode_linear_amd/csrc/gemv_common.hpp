@@ -46,6 +46,9 @@ struct GemvArgs {
   uint8_t* oc;
   uint8_t* os;
   float* og;
+  int rms;       // nonzero: RMS-normalise each row (epsilon eps) before quantizing
+  float eps;
+  float* ho;     // optional binary32 h [M][K] (workgroup 0)
 };
 
 __device__ inline u32x4 load_codes(const uint8_t* p, bool nt) {

@@ -8,8 +8,12 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
                               const uint8_t* xs, const float* xg, const uint8_t* wc,
                               const uint8_t* ws, const float* wg, void* y, int out_bf16,
                               void* workspace, hipStream_t s, const uint16_t* xb, int64_t ldx,
-                              uint8_t* oc, uint8_t* os, float* og) {
+                              uint8_t* oc, uint8_t* os, float* og, int rms, float eps,
+                              float* ho) {
   GemvArgs a = {};
+  a.rms = rms;
+  a.eps = eps;
+  a.ho = ho;
   a.xb = xb;
   a.ldx = ldx;
   a.oc = oc;

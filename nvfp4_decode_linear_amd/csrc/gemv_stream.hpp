@@ -130,7 +130,9 @@ __device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g
 // compile-time constants on every path (the paths never merge), so the
 // compiler's memory wait counts stay exact: where paths with different
 // numbers of outstanding loads merge, it waits for all of them.
-template <int M, int RG, int XS, bool MF, bool SPLIT, bool QA, bool H16>
+// QA: 0 = the activation arrives quantized; 1 = the prologue quantizes the
+// bf16 activation; 2 = it applies the unweighted per-row RMS norm first.
+template <int M, int RG, int XS, bool MF, bool SPLIT, int QA, bool H16>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   static_assert(!H16 || (MF && !SPLIT), "half tiles: MFMA kernel, one K slice");
   constexpr int GC = H16 ? 8 : 4;             // chunks per ring group
@@ -245,6 +247,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
   u32x2 xc0[QA ? 1 : kStreamXpt];             // else: its first quantized activation blocks
   uint32_t xs0[QA ? 1 : kStreamXpt];
+  static_assert(QA >= 0 && QA <= 2, "activation prologue mode");
   auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
     if constexpr (MF) {
       xlds[(m * kc * 4 + kb) * 2] = c.x;
@@ -263,23 +266,84 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // to the standalone activation quantizer's.
   // (the bf16 loads are issued before the first weight loads, so waiting for
   // them does not wait for the weights)
+  // QA == 2: h = x * (1 / sqrt(mean_k x^2 + eps)) per row in binary32 (the
+  // row sums in a fixed order: per thread its blocks in order, then the wave
+  // tree, then the waves in order, the same in every workgroup), then the
+  // quantizer on h; h is recomputed from the bf16 registers when needed, and
+  // workgroup 0 can write it out.
   auto quantize_prologue = [&]() __attribute__((always_inline)) {
     const int T = 64 * NW;
     const int nreal = M * kb_row;
     auto& v = qv;
+    uint32_t* wred = reinterpret_cast<uint32_t*>(red);
+    // the rows' 1 / rms in LDS (a register array indexed by row would be
+    // placed in scratch)
+    float* rinv = reinterpret_cast<float*>(red) + NW * M;
+    auto row_rinv = [&](int m) __attribute__((always_inline)) { return rinv[m]; };
+    auto block_h = [&](int r, float rv, float (&hb)[16]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hb[2 * e] = __fmul_rn(__uint_as_float(v[r][e] << 16), rv);
+        hb[2 * e + 1] = __fmul_rn(__uint_as_float(v[r][e] & 0xFFFF0000u), rv);
+      }
+    };
+    if constexpr (QA == 2) {
+      float ss[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) ss[m] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kQaBpt; ++r) {
+        const int i = (int)threadIdx.x + r * T;
+        const int mr = i < nreal ? i / kb_row : M;        // M: no row
+        float bs = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x0 = __uint_as_float(v[r][e] << 16);
+          const float x1 = __uint_as_float(v[r][e] & 0xFFFF0000u);
+          bs = __fadd_rn(bs, __fmul_rn(x0, x0));
+          bs = __fadd_rn(bs, __fmul_rn(x1, x1));
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) ss[m] = m == mr ? __fadd_rn(ss[m], bs) : ss[m];
+      }
+      float* wss = reinterpret_cast<float*>(red);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float w = wave_sum_f32(ss[m]);
+        if (lane == 0) wss[wave * M + m] = w;
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < M) {
+        const int m = threadIdx.x;
+        float t = wss[m];
+        for (int w = 1; w < NW; ++w) t = __fadd_rn(t, wss[w * M + m]);
+        const float ms = __fdiv_rn(t, (float)a.K);
+        rinv[m] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, a.eps)));
+      }
+      __syncthreads();                                  // wss is reused below
+    }
     uint32_t amax = 0;
 #pragma unroll
     for (int r = 0; r < kQaBpt; ++r) {      // branch free: exact wait counts
-      const uint32_t b = absmax_bits(v[r]);
-      amax = max(amax, (int)threadIdx.x + r * T < nreal ? b : 0u);
+      const int i = (int)threadIdx.x + r * T;
+      uint32_t b;
+      if constexpr (QA == 2) {
+        float hb[16];
+        block_h(r, row_rinv(i < nreal ? i / kb_row : 0), hb);
+        b = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) b = max(b, __float_as_uint(hb[e]) & 0x7FFFFFFFu);
+      } else {
+        b = absmax_bits(v[r]);
+      }
+      amax = max(amax, i < nreal ? b : 0u);
     }
     amax = wave_max_u32(amax);
-    uint32_t* wmax = reinterpret_cast<uint32_t*>(red);
-    if (lane == 0) wmax[wave] = amax;
+    if (lane == 0) wred[wave] = amax;
     __syncthreads();
     amax = 0;
-    for (int w = 0; w < NW; ++w) amax = max(amax, wmax[w]);
-    const float sg = tensor_scale(bf16_to_f32(amax));
+    for (int w = 0; w < NW; ++w) amax = max(amax, wred[w]);
+    const float sg = tensor_scale(QA == 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
     g = __fmul_rn(sg, a.wg[0]);
     const bool out = blockIdx.x == 0;
 #pragma unroll
@@ -287,7 +351,20 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       const int i = (int)threadIdx.x + r * T;
       if (i < nreal) {
         const int m = i / kb_row, kb = i - m * kb_row;
-        const BlockQ q = quantize_block_bf16(v[r], sg);
+        BlockQ q;
+        if constexpr (QA == 2) {
+          float hb[16];
+          block_h(r, row_rinv(m), hb);
+          q = quantize_block_f32(hb, sg);
+          if (out && a.ho) {
+            float4* o = reinterpret_cast<float4*>(a.ho + (int64_t)m * a.K + 16 * kb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[e] = make_float4(hb[4 * e], hb[4 * e + 1], hb[4 * e + 2], hb[4 * e + 3]);
+          }
+        } else {
+          q = quantize_block_bf16(v[r], sg);
+        }
         put(m, kb, u32x2{q.lo, q.hi}, q.scale);
         if (out) {
           *reinterpret_cast<u32x2*>(a.oc + (int64_t)m * (a.K >> 1) + 8 * kb) = u32x2{q.lo, q.hi};
@@ -594,16 +671,16 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 template <int M, bool SPLIT>
 __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, stream_ring_groups(M), 0, false, SPLIT, false, false>(a, lds);
+  stream_body<M, stream_ring_groups(M), 0, false, SPLIT, 0, false>(a, lds);
 }
 
-template <int M, bool SPLIT, bool QA, bool H16>
+template <int M, bool SPLIT, int QA, bool H16>
 __global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
   stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA, H16>(a, lds);
 }
 
-template <int M, bool MF, bool SPLIT, bool QA, bool H16>
+template <int M, bool MF, bool SPLIT, int QA, bool H16>
 hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch, H16 ? kTileN / 2 : kTileN);
   const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
@@ -629,19 +706,24 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
     return hipErrorInvalidValue;
   if constexpr (MF) {
+    if (a.xb && M * (a.K >> 4) > kQaBpt * 64 * p.waves) return hipErrorInvalidValue;
+    const int qa = a.xb ? (a.rms ? 2 : 1) : 0;
     if (p.h16) {
       if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
-      return a.xb ? launch_ms<M, true, false, true, true>(p, a, s)
-                  : launch_ms<M, true, false, false, true>(p, a, s);
+      return qa == 2   ? launch_ms<M, true, false, 2, true>(p, a, s)
+             : qa == 1 ? launch_ms<M, true, false, 1, true>(p, a, s)
+                       : launch_ms<M, true, false, 0, true>(p, a, s);
     }
-    if (a.xb) {
-      if (M * (a.K >> 4) > kQaBpt * 64 * p.waves) return hipErrorInvalidValue;
-      return p.splits > 1 ? launch_ms<M, true, true, true, false>(p, a, s)
-                          : launch_ms<M, true, false, true, false>(p, a, s);
+    if (qa) {
+      if (p.splits > 1)
+        return qa == 2 ? launch_ms<M, true, true, 2, false>(p, a, s)
+                       : launch_ms<M, true, true, 1, false>(p, a, s);
+      return qa == 2 ? launch_ms<M, true, false, 2, false>(p, a, s)
+                     : launch_ms<M, true, false, 1, false>(p, a, s);
     }
   }
-  return p.splits > 1 ? launch_ms<M, MF, true, false, false>(p, a, s)
-                      : launch_ms<M, MF, false, false, false>(p, a, s);
+  return p.splits > 1 ? launch_ms<M, MF, true, 0, false>(p, a, s)
+                      : launch_ms<M, MF, false, 0, false>(p, a, s);
 }
 
 }  // namespace

@@ -90,7 +90,8 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               int out_bf16, void* workspace, hipStream_t s,
                               const uint16_t* xb = nullptr, int64_t ldx = 0,
                               uint8_t* oc = nullptr, uint8_t* os = nullptr,
-                              float* og = nullptr);
+                              float* og = nullptr, int rms = 0, float eps = 0.0f,
+                              float* ho = nullptr);
 
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
 // (4 bf16 blocks per thread).

@@ -73,20 +73,24 @@ nvfp4_status enqueue_step(nvfp4_stack* s, void* st) {
     const nvfp4_weight* w = &s->w[(size_t)l * 4];
     const uint16_t* xin = l == 0 ? s->x_in : s->h;
     uint16_t* xout = l == c.layers - 1 ? s->y_out : s->h;
-    if ((r = nvfp4_rmsnorm_quantize_act(xin, M, c.hidden, c.hidden, c.eps, s->a_codes, s->a_scales,
-                                        s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) != NVFP4_OK)
+    // RMS norm + quantize + QKV (one kernel when it fits)
+    if ((r = nvfp4_rmsnorm_quantize_linear(M, c.qkv_n, c.hidden, xin, c.hidden, c.eps,
+                                           w[kQkv].codes, w[kQkv].scales, w[kQkv].gscale, s->qkv,
+                                           NVFP4_OUT_BF16, s->a_codes, s->a_scales, s->a_gscale,
+                                           nullptr, s->ws, s->ws_bytes, st)) != NVFP4_OK)
       break;
-    if ((r = lin(w[kQkv], c.qkv_n, c.hidden, s->qkv)) != NVFP4_OK) break;
     // quantize the q columns and apply O (one kernel when it fits)
     if ((r = nvfp4_quantize_linear(M, c.hidden, c.q_cols, s->qkv, c.qkv_n, w[kO].codes,
                                    w[kO].scales, w[kO].gscale, s->o, NVFP4_OUT_BF16, s->a_codes,
                                    s->a_scales, s->a_gscale, s->ws, s->ws_bytes, st)) != NVFP4_OK)
       break;
-    if ((r = nvfp4_rmsnorm_quantize_act(s->o, M, c.hidden, c.hidden, c.eps, s->a_codes,
-                                        s->a_scales, s->a_gscale, nullptr, s->ws, s->ws_bytes,
-                                        st)) != NVFP4_OK)
+    // RMS norm + quantize + gate_up (one kernel when it fits)
+    if ((r = nvfp4_rmsnorm_quantize_linear(M, 2 * c.ffn, c.hidden, s->o, c.hidden, c.eps,
+                                           w[kGateUp].codes, w[kGateUp].scales,
+                                           w[kGateUp].gscale, s->gu, NVFP4_OUT_BF16, s->a_codes,
+                                           s->a_scales, s->a_gscale, nullptr, s->ws, s->ws_bytes,
+                                           st)) != NVFP4_OK)
       break;
-    if ((r = lin(w[kGateUp], 2 * c.ffn, c.hidden, s->gu)) != NVFP4_OK) break;
     if ((r = nvfp4_silu_mul_quantize_act(s->gu, M, c.ffn, 2 * c.ffn, s->a_codes, s->a_scales,
                                          s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) !=
         NVFP4_OK)
@@ -132,9 +136,9 @@ nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weigh
   hipError_t e = hipGetDevice(&s->device);
   const int64_t kmax = std::max({c.hidden, c.q_cols, c.ffn});
   size_t ws = 256;
-  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.qkv_n, c.hidden));
+  ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, c.qkv_n, c.hidden));
   ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, c.hidden, c.q_cols));
-  ws = std::max(ws, nvfp4_linear_workspace_bytes(M, 2 * c.ffn, c.hidden));
+  ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, 2 * c.ffn, c.hidden));
   ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.ffn));
   s->ws_bytes = ws;
   auto alloc = [&](auto** p, size_t bytes) {

@@ -110,3 +110,40 @@ def test_fused_strided_input_and_graph_replay(nv):
         _sync()
         assert _same(y, y0), f"replay {r}"
         assert _same(q.codes, xq.codes) and _same(q.scales, xq.scales)
+
+
+RMS_SHAPES = [(6144, 4096, 1), (24576, 4096, 2), (10240, 5120, 1), (10240, 5120, 3),
+              (51200, 5120, 1), (10240, 5120, 8), (100, 1040, 3), (33, 16, 8)]
+U32 = 2.0 ** -24
+
+
+@pytest.mark.parametrize("N,K,M", RMS_SHAPES)
+def test_rmsnorm_quantize_linear(nv, half_tiles, N, K, M):
+    """RMS norm, quantization and the linear in one call (one kernel up to
+    1600 activation blocks, else the standalone fused quantizer and the
+    linear): h within the binary32 bound of the oracle, the codes exactly
+    the oracle quantizer of that h, y bit-identical to the linear alone on
+    the written quantized activation."""
+    import torch
+    note(f"rmsnorm_quantize_linear N={N} K={K} M={M}")
+    w16 = weights_bf16(9, N % 7, N, K)
+    x16 = activations_bf16(9, K % 5, M, K, "student_t")
+    wq = nv.quantize_weight(to_dev_bf16(w16))
+    x = to_dev_bf16(x16)
+    h = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    y, q = nv.rmsnorm_quantize_linear(x, wq, 1e-6, out_dtype=torch.bfloat16, h_out=h)
+    _sync()
+    hn = h.cpu().numpy()
+    ref = oracle.rms_norm_rows(bf16_to_f32(x16).astype(np.float64))
+    # row sums: <= 64 sequential adds per thread (4 blocks), a 6-level wave
+    # tree, <= 7 adds over the waves: 40 u covers the square root and the
+    # five correctly rounded steps, as for the standalone quantizer
+    assert np.all(np.abs(hn - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
+    oq = oracle.quantize(hn)
+    assert np.array_equal(q.codes.cpu().numpy(), oq.codes)
+    assert np.array_equal(q.scales.cpu().numpy(), oq.scales)
+    assert q.gscale.cpu().numpy().view(np.uint32)[0] == np.asarray(oq.gscale,
+                                                                   np.float32).view(np.uint32)
+    y0 = nv.linear(q, wq, out_dtype=torch.bfloat16)
+    _sync()
+    assert _same(y, y0)

@@ -48,8 +48,10 @@ def _weights(nv, cfg):
 
 
 def _eager(nv, cfg, wq, x, trace=False):
-    """The step op by op through the binding; with trace, the inputs and
-    outputs of every op of every layer."""
+    """The step call by call through the binding (the calls the stack makes:
+    RMS norm + quantize + QKV, quantize + O, RMS norm + quantize + gate_up,
+    SiLU * mul + quantize, down); with trace, the inputs and outputs of every
+    op of every layer."""
     import torch
     M, hidden, qkv_n, q_cols, ffn, layers = cfg
     ops = []
@@ -57,13 +59,10 @@ def _eager(nv, cfg, wq, x, trace=False):
     for l in range(layers):
         qkv_w, o_w, gu_w, dn_w = wq[l]
         h1 = torch.empty((M, hidden), dtype=torch.float32, device="cuda")
-        a1 = nv.rmsnorm_quantize_act(cur, 1e-6, h_out=h1)
-        qkv = nv.linear(a1, qkv_w, out_dtype=torch.bfloat16)
-        a2 = nv.quantize_act(qkv[:, :q_cols])
-        o = nv.linear(a2, o_w, out_dtype=torch.bfloat16)
+        qkv, a1 = nv.rmsnorm_quantize_linear(cur, qkv_w, 1e-6, out_dtype=torch.bfloat16, h_out=h1)
+        o, a2 = nv.quantize_linear(qkv[:, :q_cols], o_w, out_dtype=torch.bfloat16)
         h3 = torch.empty((M, hidden), dtype=torch.float32, device="cuda")
-        a3 = nv.rmsnorm_quantize_act(o, 1e-6, h_out=h3)
-        gu = nv.linear(a3, gu_w, out_dtype=torch.bfloat16)
+        gu, a3 = nv.rmsnorm_quantize_linear(o, gu_w, 1e-6, out_dtype=torch.bfloat16, h_out=h3)
         h4 = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
         a4 = nv.silu_mul_quantize_act(gu, h_out=h4)
         dn = nv.linear(a4, dn_w, out_dtype=torch.bfloat16)
