@@ -205,6 +205,11 @@ class Timer:
         return e0.elapsed_time(e1) / n
 
 
+def progress(msg):
+    """One line on stderr per finished phase, so a long run shows progress."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +288,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    progress(f"timed step: {args.steps} replays, {ms_step * 1e3:.2f} us per step")
     step_bytes = sum(step_linear_bytes(M, L.N, L.K) for L in linears)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     del step_graphs
@@ -326,6 +332,8 @@ def main():
                              "act_quant_us": round(us_q, 3)})
                 del g, gq, gf
             table[f"M{Mx}"] = rows
+            progress(f"per-linear table M={Mx}: " + ", ".join(
+                f"{r['name']} {r['us']:.2f}/{r['linear_only_us']:.2f} us" for r in rows))
         return table
 
     sweep_ms = (M,) if args.no_extras else tuple(sorted({M, 1, 2, 4, 8}))
@@ -344,6 +352,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(linears, cfg, M, kind, args.cpu_seconds)
+        progress(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads")
 
     out = {
         "metric": "NVFP4 W4A4 GEMV achieved HBM GB/s (% of peak) + us per linear at M=1,2,4,8",
@@ -435,6 +444,7 @@ def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
                            "replays": args.stack_steps, "output_finite": finite}
         st.close()
         del st
+        progress(f"stack M={Mx}: {ms * 1e3:.1f} us per step")
     return {"linears_32b": lin32, "stack_qwen3_32b": stack}
 
 

@@ -24,7 +24,7 @@ TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                      "(python -m nvfp4_decode_linear_amd.build)")
+                      "(python nvfp4_decode_linear_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

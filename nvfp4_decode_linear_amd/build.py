@@ -2,7 +2,7 @@
 
 Compiles every source under csrc/ in-tree (object files under _build/) and
 links the shared library next to this file.  Run as
-``python -m nvfp4_decode_linear_amd.build`` or through
+``python nvfp4_decode_linear_amd/build.py`` or through
 ``__graft_entry__.build()``.
 """
 
