@@ -270,6 +270,15 @@ size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K);
  * be used by two calls that can run concurrently. */
 nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device self-check of the E2M1 encoder the quantizers use (gfx950's packed
+ * FP4 conversion at unit scale) against the rounding rule stated above
+ * (nearest, ties to the even code, saturating at 6, sign bit from the input):
+ * every finite binary32 pattern is encoded both ways, paired with its
+ * negation.  result: 2 device uint64 (8-byte aligned), overwritten with
+ * {patterns that differ, patterns checked}; expect {0, 2^32 - 2^24}.
+ * Errors: NVFP4_ERR_INVALID_ARG for a null or misaligned result. */
+nvfp4_status nvfp4_selftest_e2m1(unsigned long long* result, void* stream);
+
 /* The decode linear y[m][n] = xgs * wgs * sum_k x[m][k] w[n][k] over the
  * dequantized NVFP4 operands, 1 <= M <= 8, N <= 524288.
  *   x_codes/x_scales canonical activation ([M][K/2], [M][K/16]); x_gscale

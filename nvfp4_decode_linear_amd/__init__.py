@@ -58,6 +58,7 @@ _silu_mul_quantize_act = _sig("nvfp4_silu_mul_quantize_act", _c_int, _vp, _c_int
                               _vp, _vp, _vp, _vp, _vp, _c_size, _vp)
 _linear_workspace_bytes = _sig("nvfp4_linear_workspace_bytes", _c_size, _c_int, _c_i64, _c_i64)
 _workspace_init = _sig("nvfp4_workspace_init", _c_int, _vp, _c_size, _vp)
+_selftest_e2m1 = _sig("nvfp4_selftest_e2m1", _c_int, _vp, _vp)
 _linear = _sig("nvfp4_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                _c_int, _vp, _c_size, _vp)
 _quantize_linear = _sig("nvfp4_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp, _c_i64, _vp,
@@ -169,6 +170,16 @@ def quantize_weight(w, out: QuantWeight | None = None) -> QuantWeight:
     _check(_quantize_weight(_ptr(w), N, K, w.stride(0), _ptr(q.codes), _ptr(q.scales),
                             _ptr(q.gscale), _stream(w)), "nvfp4_quantize_weight")
     return q
+
+
+def selftest_e2m1(device="cuda"):
+    """(mismatches, checked) of the device E2M1 encoder against its rounding
+    rule over every finite binary32 pattern (nvfp4_selftest_e2m1)."""
+    torch = _torch()
+    out = torch.empty(2, dtype=torch.int64, device=device)
+    _check(_selftest_e2m1(_ptr(out), _stream(out)), "nvfp4_selftest_e2m1")
+    v = out.cpu().tolist()
+    return v[0], v[1]
 
 
 def unpack_weight(q: QuantWeight):

@@ -459,6 +459,13 @@ size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {
   return make_plan(M, N, K).ws_bytes;
 }
 
+nvfp4_status nvfp4_selftest_e2m1(unsigned long long* result, void* stream) {
+  if (!result || !aligned(result, 8)) return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_e2m1_selftest(result, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
 nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (workspace_bytes == 0) return NVFP4_OK;
   if (!workspace || !aligned(workspace, 4)) return NVFP4_ERR_INVALID_ARG;

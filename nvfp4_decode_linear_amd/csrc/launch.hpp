@@ -79,6 +79,9 @@ hipError_t launch_unpack_weight(const uint8_t* codes, const uint8_t* scales, int
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// Exhaustive check of the instruction E2M1 encoder (out: 2 x u64).
+hipError_t launch_e2m1_selftest(unsigned long long* out, hipStream_t s);
+
 hipError_t launch_gemv_split(const GemvPlan& p, int M, int64_t N, int64_t K,
                              const uint8_t* xc, const uint8_t* xs, const float* xg,
                              const uint8_t* wc, const uint8_t* ws, const float* wg, void* y,

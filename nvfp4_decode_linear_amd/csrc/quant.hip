@@ -385,6 +385,28 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
   scales_rm[n * nbr + j] = scales[(t * kg + g) * kScaleRecord + 8 * l + 2 * q + b];
 }
 
+// Every finite binary32 pattern (exponent field below 255), each paired with
+// its negation: the instruction encoder e2m1x2 against the rounding rule
+// f32_to_e2m1_rne_sat.  out[0] += mismatching patterns, out[1] += patterns
+// checked.  Thread t covers patterns [t * per, (t + 1) * per).
+__global__ __launch_bounds__(256) void e2m1_selftest_kernel(unsigned long long* out,
+                                                            uint64_t per) {
+  const uint64_t beg = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * per;
+  unsigned long long bad = 0, seen = 0;
+  for (uint64_t k = 0; k < per; ++k) {
+    const uint64_t idx = beg + k;
+    if (idx >> 32) break;
+    const uint32_t u = (uint32_t)idx;
+    if ((u & 0x7F800000u) == 0x7F800000u) continue;
+    const float y = __uint_as_float(u), z = __uint_as_float(u ^ 0x80000000u);
+    const uint32_t ref = f32_to_e2m1_rne_sat(y) | (f32_to_e2m1_rne_sat(z) << 4);
+    bad += e2m1x2(y, z) != ref;
+    ++seen;
+  }
+  atomicAdd(out, bad);
+  atomicAdd(out + 1, seen);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t words) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
     p[i] = 0u;
@@ -480,6 +502,15 @@ hipError_t launch_unpack_weight(const uint8_t* codes, const uint8_t* scales, int
   const int64_t total = N * (K >> 4);
   hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, codes,
                      scales, N, K, kc, kg, codes_rm, scales_rm);
+  return hipGetLastError();
+}
+
+hipError_t launch_e2m1_selftest(unsigned long long* out, hipStream_t s) {
+  hipError_t e = launch_fill_zero(out, 16, s);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = 8192, threads = 256;           // 2^21 threads x 2048 = 2^32
+  hipLaunchKernelGGL(e2m1_selftest_kernel, dim3(blocks), dim3(threads), 0, s, out,
+                     (uint64_t)1 << 11);
   return hipGetLastError();
 }
 

@@ -103,6 +103,17 @@ def _tie_suite(q=0, width=16 * 160):
     return bf16_bits(x)
 
 
+def test_e2m1_instruction_encoder_exhaustive(nv):
+    """The quantizers round y = x * r to E2M1 with gfx950's packed FP4
+    conversion at unit scale.  Over every finite binary32 pattern (and its
+    negation) it must give the code of the stated rounding rule: nearest,
+    ties to the even code, saturating at 6, sign bit from y."""
+    note("e2m1 encoder self-check over all finite binary32 patterns")
+    bad, seen = nv.selftest_e2m1()
+    assert seen == (1 << 32) - (1 << 24)
+    assert bad == 0
+
+
 def test_act_quant_ties_and_every_scale_byte(nv):
     x = _tie_suite()
     assert x.shape[0] <= 8
