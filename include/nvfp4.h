@@ -190,7 +190,7 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
  * bit-identical to nvfp4_quantize_act(x_bf16 -> x_codes, x_scales,
  * x_gscale) followed by nvfp4_linear on those outputs, which this call also
  * writes.  When the plan streams the weights on the MFMA kernel and M * K /
- * 16 <= 1600, a single kernel does both: every workgroup quantizes the
+ * 16 <= 2048, a single kernel does both: every workgroup quantizes the
  * activation in its prologue (reading the bf16 input from L2) and workgroup
  * 0 writes the quantized copy, so the separate quantizer launch disappears;
  * otherwise (or with NVFP4_OPT_FUSE_QUANT = 0) the two launches run in

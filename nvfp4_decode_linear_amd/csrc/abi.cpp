@@ -81,7 +81,7 @@ bool split_ok(int M, int cpw, int waves) {
 }
 
 constexpr int64_t kLdsBudget = 160 * 1024;
-constexpr int64_t kFuseMaxBlocks = 1600;
+constexpr int64_t kFuseMaxBlocks = 2048;
 
 void finish_workspace(GemvPlan& p, int M) {
   // The arrival counters live in a fixed region at the start of the
@@ -134,8 +134,8 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
   const bool want_valu = !want_mfma && (force_kernel == 1 || auto_kind) && M <= 3;
   if (want_mfma || want_valu) {
     const int max_waves = want_mfma ? 8 : (M == 1 ? 16 : 8);  // as compiled
-    const int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves)
-                                     : std::min(max_waves, 8);
+    int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves)
+                               : std::min(max_waves, 8);
     // 16-row half tiles (MFMA only, one K slice): twice the work items, for
     // shapes whose 32-row tiles leave CUs idle.
     const int64_t force_half = g_opts[NVFP4_OPT_HALF_TILES].load();
@@ -144,14 +144,35 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     const int gc = h16 ? 8 : 4;                              // chunks per ring group
     const int s0 = h16 ? 1 : force_split > 0 ? (int)force_split : stream_splits(p.tiles, p.kc);
     const int kcs = (p.kc + s0 - 1) / s0;                 // chunks per slice
-    const int cpw = (int)round_up((kcs + want - 1) / want, gc);
-    const int waves = (kcs + cpw - 1) / cpw;
-    const int cps = cpw * waves;
-    const int splits = (p.kc + cps - 1) / cps;
-    const int64_t items = (int64_t)p.tiles * (h16 ? 2 : 1) * splits;
     const int64_t force_grid = g_opts[NVFP4_OPT_GRID].load();
-    const int grid = (int)std::min<int64_t>(items, force_grid > 0 ? force_grid : kStreamGrid);
-    const int64_t per_wg = (items + grid - 1) / grid;
+    int cpw, waves, cps, splits, grid;
+    int64_t items, per_wg;
+    auto shape = [&]() {
+      cpw = (int)round_up((kcs + want - 1) / want, gc);
+      waves = (kcs + cpw - 1) / cpw;
+      cps = cpw * waves;
+      splits = (p.kc + cps - 1) / cps;
+      items = (int64_t)p.tiles * (h16 ? 2 : 1) * splits;
+      grid = (int)std::min<int64_t>(items, force_grid > 0 ? force_grid : kStreamGrid);
+      per_wg = (items + grid - 1) / grid;
+    };
+    shape();
+    // One activation row on the MFMA dot: when every workgroup
+    // streams about the same amount (>= 85% of a whole number of rounds) and
+    // each wave would run through its whole ring of loads, half the waves
+    // with twice the stream each measured faster (less data in flight per
+    // CU: Qwen3-8B down 8.4 against 9.3 us, Qwen3-32B gate_up 29.5 against
+    // 30.6 us); at 8 rows the dot needs the waves (every shape slower).  Kept
+    // only where the activation still fits the 4-wave quantizing prologue.
+    if (force_waves == 0 && want_mfma && M == 1 && splits == 1 &&
+        (int64_t)M * (p.kc * 4) <= nvfp4::qa_max_blocks(4)) {
+      const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
+      const bool even = items * 100 >= rounds * kStreamGrid * 85;
+      if (even && per_wg * (cpw / gc) >= 3) {          // 3: the ring depth at M = 1
+        want = 4;
+        shape();
+      }
+    }
     const int64_t act = (int64_t)nvfp4::stream_act_lds(M, p.kc, want_mfma);
     const int64_t slot = (int64_t)waves * M * (h16 ? 16 : 32) * 4;
     const int64_t batch = std::min<int64_t>(per_wg, (kLdsBudget - act) / slot);
@@ -359,8 +380,9 @@ nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, int M, int64
     return NVFP4_ERR_INVALID_ARG;
   const GemvPlan p = make_plan(M, N, K);
   // Every workgroup quantizes the whole activation in its prologue: worth it
-  // up to ~1600 blocks (measured: M * K / 16 = 2048 runs slower fused than
-  // as two launches).
+  // up to 2048 blocks (4 per thread), since the E2M1 encoding runs on the
+  // conversion instruction (with the compare-chain encoder, 2048 blocks ran
+  // slower fused than as two launches).
   const int64_t blocks = (int64_t)M * (K >> 4);
   const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
                      blocks <= nvfp4::qa_max_blocks(p.waves) && blocks <= kFuseMaxBlocks;

@@ -120,7 +120,7 @@ U32 = 2.0 ** -24
 @pytest.mark.parametrize("N,K,M", RMS_SHAPES)
 def test_rmsnorm_quantize_linear(nv, half_tiles, N, K, M):
     """RMS norm, quantization and the linear in one call (one kernel up to
-    1600 activation blocks, else the standalone fused quantizer and the
+    2048 activation blocks, else the standalone fused quantizer and the
     linear): h within the binary32 bound of the oracle, the codes exactly
     the oracle quantizer of that h, y bit-identical to the linear alone on
     the written quantized activation."""
