@@ -83,6 +83,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   StaticFor<0, N>::run(f);
 }
 
+// Row of flat block index i (0 <= i < M * per_row) of an M-row activation:
+// i / per_row by M - 1 comparisons (a runtime integer division costs about
+// 20 VALU instructions, and the prologue needs several per thread).
+template <int M>
+__device__ __forceinline__ int row_of(int i, int per_row) {
+  int m = 0;
+#pragma unroll
+  for (int j = 1; j < M; ++j) m += i >= j * per_row ? 1 : 0;
+  return m;
+}
+
 // Split-K tail of the streaming kernels, after the workgroup's last item:
 // wait until its partial sums are stored, count each of its items in at its
 // row tile's arrival counter (thread j takes item j, so the atomics overlap),
@@ -293,8 +304,9 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       for (int m = 0; m < M; ++m) ss[m] = 0.0f;
 #pragma unroll
       for (int r = 0; r < kQaBpt; ++r) {
+        if (r > 0 && nreal <= r * T) break;           // uniform: no block r here
         const int i = (int)threadIdx.x + r * T;
-        const int mr = i < nreal ? i / kb_row : M;        // M: no row
+        const int mr = i < nreal ? row_of<M>(i, kb_row) : M;   // M: no row
         float bs = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -324,12 +336,13 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
     uint32_t amax = 0;
 #pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {      // branch free: exact wait counts
+    for (int r = 0; r < kQaBpt; ++r) {
+      if (r > 0 && nreal <= r * T) break;             // uniform: no block r here
       const int i = (int)threadIdx.x + r * T;
       uint32_t b;
       if constexpr (QA == 2) {
         float hb[16];
-        block_h(r, row_rinv(i < nreal ? i / kb_row : 0), hb);
+        block_h(r, row_rinv(i < nreal ? row_of<M>(i, kb_row) : 0), hb);
         b = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) b = max(b, __float_as_uint(hb[e]) & 0x7FFFFFFFu);
@@ -350,7 +363,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     for (int r = 0; r < kQaBpt; ++r) {
       const int i = (int)threadIdx.x + r * T;
       if (i < nreal) {
-        const int m = i / kb_row, kb = i - m * kb_row;
+        const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
         BlockQ q;
         if constexpr (QA == 2) {
           float hb[16];
@@ -389,7 +402,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     for (int r = 0; r < kStreamXpt; ++r) {
       const int i = threadIdx.x + r * 64 * NW;
       if (i < nblk) {
-        const int m = i / (kc * 4), kb = i - m * (kc * 4);
+        const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
         const bool ok = kb < kb_row;
         put(m, kb, ok ? xc0[r] : u32x2{0u, 0u}, ok ? xs0[r] : 0u);
       }
@@ -403,7 +416,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 #pragma unroll
       for (int r = 0; r < kStreamXrest; ++r) {
         const int i = min(base + r * 64 * NW, nblk - 1);
-        const int m = i / (kc * 4), kb = i - m * (kc * 4);
+        const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
         const int kbc = min(kb, kb_row - 1);
         c[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kbc);
         sc[r] = a.xs[(int64_t)m * kb_row + kbc];
@@ -412,7 +425,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       for (int r = 0; r < kStreamXrest; ++r) {
         const int i = base + r * 64 * NW;
         if (i < nblk) {
-          const int m = i / (kc * 4), kb = i - m * (kc * 4);
+          const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
           const bool ok = kb < kb_row;
           put(m, kb, ok ? c[r] : u32x2{0u, 0u}, ok ? sc[r] : 0u);
         }
@@ -535,7 +548,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = 2 * mp + (v >> 1), b = v & 1;
-          if (m < M) acc[m] = fmaf(C[v], (float)sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
+          if (m < M) acc[m] = fmaf(C[v], fmaf((float)sap[b * M + m], b ? sw1 : sw0, 0.0f), acc[m]);
         }
       }
     }
@@ -573,7 +586,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         for (int v = 0; v < 16; ++v) {
           const int m = 2 * (v >> 2) + ((v & 3) >> 1), b = v & 1;
           if constexpr (true) {
-            if (m < M) acc[m] = fmaf(C[v], (float)sap[b * M + m] * (b ? sw1 : sw0), acc[m]);
+            if (m < M) acc[m] = fmaf(C[v], fmaf((float)sap[b * M + m], b ? sw1 : sw0, 0.0f), acc[m]);
           }
         }
       } else {
@@ -628,17 +641,21 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   if constexpr (QA) {
     const int T = 64 * NW;
     const int nreal = M * kb_row;
+    // only the rounds of T blocks the activation has (a uniform branch: the
+    // weight loads that follow are issued after all of these on every path,
+    // so no wait for an activation block waits for a weight load)
 #pragma unroll
     for (int r = 0; r < kQaBpt; ++r) {
+      if (r > 0 && nreal <= r * T) break;
       const int i = min((int)threadIdx.x + r * T, nreal - 1);
-      const int m = i / kb_row, kb = i - m * kb_row;
+      const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
       load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
     }
   } else {
 #pragma unroll
     for (int r = 0; r < kStreamXpt; ++r) {
       const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
-      const int m = i / (kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
+      const int m = row_of<M>(i, kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
       xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
       xs0[r] = a.xs[(int64_t)m * kb_row + kb];
     }
