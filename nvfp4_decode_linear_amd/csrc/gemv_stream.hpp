@@ -335,6 +335,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       __syncthreads();                                  // wss is reused below
     }
     uint32_t amax = 0;
+    uint32_t bmx[kQaBpt];                    // each block's largest magnitude, reused below
 #pragma unroll
     for (int r = 0; r < kQaBpt; ++r) {
       if (r > 0 && nreal <= r * T) break;             // uniform: no block r here
@@ -349,6 +350,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       } else {
         b = absmax_bits(v[r]);
       }
+      bmx[r] = b;
       amax = max(amax, i < nreal ? b : 0u);
     }
     amax = wave_max_u32(amax);
@@ -368,7 +370,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         if constexpr (QA == 2) {
           float hb[16];
           block_h(r, row_rinv(m), hb);
-          q = quantize_block_f32(hb, sg);
+          q = quantize_block_f32(hb, __uint_as_float(bmx[r]), sg);
           if (out && a.ho) {
             float4* o = reinterpret_cast<float4*>(a.ho + (int64_t)m * a.K + 16 * kb);
 #pragma unroll
@@ -376,7 +378,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
               o[e] = make_float4(hb[4 * e], hb[4 * e + 1], hb[4 * e + 2], hb[4 * e + 3]);
           }
         } else {
-          q = quantize_block_bf16(v[r], sg);
+          q = quantize_block_bf16(v[r], bmx[r], sg);
         }
         put(m, kb, u32x2{q.lo, q.hi}, q.scale);
         if (out) {
@@ -400,6 +402,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
 #pragma unroll
     for (int r = 0; r < kStreamXpt; ++r) {
+      if (r > 0 && nblk <= r * 64 * NW) break;        // rounds that were loaded
       const int i = threadIdx.x + r * 64 * NW;
       if (i < nblk) {
         const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
@@ -654,6 +657,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   } else {
 #pragma unroll
     for (int r = 0; r < kStreamXpt; ++r) {
+      if (r > 0 && nblk <= r * 64 * NW) break;        // uniform, as above
       const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
       const int m = row_of<M>(i, kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
       xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);

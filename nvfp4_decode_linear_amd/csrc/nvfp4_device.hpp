@@ -105,13 +105,9 @@ struct BlockQ {
 // Quantize one 16-element block of bf16 values (8 packed pairs) given the
 // tensor scale: sigma = a / (sg*6); scale = E4M3(sigma); T = S*sg;
 // r = 1/T (0 if T == 0); code_i = E2M1(x_i * r).
-__device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], float sg) {
-  uint32_t amax_bits = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a = v[i] & 0x7FFF7FFFu;          // |x| as ordered integers
-    amax_bits = max(amax_bits, max(a & 0xFFFFu, a >> 16));
-  }
+// The block's largest magnitude (absmax_bits(v), a bf16 pattern) may be
+// passed in when the caller already has it.
+__device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], uint32_t amax_bits, float sg) {
   const float a = __uint_as_float(amax_bits << 16);
   const float d = __fmul_rn(sg, 6.0f);
   const uint32_t sb = f32_to_e4m3_rne_sat(__fdiv_rn(a, d));
@@ -131,11 +127,13 @@ __device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], float sg) {
   return q;
 }
 
-// Same for a block given as 16 binary32 values (fused stack kernels).
-__device__ inline BlockQ quantize_block_f32(const float (&x)[16], float sg) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+__device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], float sg) {
+  return quantize_block_bf16(v, absmax_bits(v), sg);
+}
+
+// Same for a block given as 16 binary32 values (fused stack kernels); a is
+// the block's largest magnitude.
+__device__ inline BlockQ quantize_block_f32(const float (&x)[16], float a, float sg) {
   const float d = __fmul_rn(sg, 6.0f);
   const uint32_t sb = f32_to_e4m3_rne_sat(__fdiv_rn(a, d));
   const float T = __fmul_rn(e4m3_to_f32(sb), sg);
@@ -149,6 +147,13 @@ __device__ inline BlockQ quantize_block_f32(const float (&x)[16], float sg) {
   q.lo = w[0];
   q.hi = w[1];
   return q;
+}
+
+__device__ inline BlockQ quantize_block_f32(const float (&x)[16], float sg) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+  return quantize_block_f32(x, a, sg);
 }
 
 // ---------------------------------------------------------- reductions
