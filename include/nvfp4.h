@@ -245,9 +245,12 @@ nvfp4_status nvfp4_rmsnorm_quantize_linear(int M, int64_t N, int64_t K, const ui
  *   h_out    optional (NULL: not written) binary32 [M][K], 16-byte aligned:
  *            the h that was quantized
  *   workspace at least 16 bytes when M > 1 (the same zero-initialised record
- *            nvfp4_quantize_act uses; it is left zero).
- * One workgroup per row; the rows' maxima are combined as in
- * nvfp4_quantize_act. */
+ *            nvfp4_quantize_act uses; it is left zero).  Optional at M = 1.
+ * rmsnorm: one workgroup per row; the rows' maxima are combined as in
+ * nvfp4_quantize_act.  silu_mul: with a workspace (any M) the M * K / 16
+ * blocks are spread over workgroups of 256 threads, one block per thread,
+ * and their maxima combined the same way; without one (M = 1) a single
+ * workgroup does the row.  Both give the same h and codes. */
 nvfp4_status nvfp4_rmsnorm_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
                                         float eps, uint8_t* x_codes, uint8_t* x_scales,
                                         float* x_gscale, float* h_out, void* workspace,

@@ -461,9 +461,15 @@ nvfp4_status prep_quantize(int mode, const uint16_t* x, int M, int64_t K, int64_
     if (!workspace || !aligned(workspace, 16)) return NVFP4_ERR_INVALID_ARG;
     if (workspace_bytes < nvfp4::kActSyncBytes) return NVFP4_ERR_WORKSPACE;
   }
+  // One row without a (large enough, aligned) workspace: no sync record, so
+  // the one-workgroup-per-row kernel runs; with one, SiLU * mul spreads its
+  // blocks over workgroups.
+  uint32_t* sync = workspace && aligned(workspace, 16) && workspace_bytes >= nvfp4::kActSyncBytes
+                       ? static_cast<uint32_t*>(workspace)
+                       : nullptr;
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
   const hipError_t e = nvfp4::launch_prep_quantize(
-      mode, x, M, (int)K, ld, eps, codes, scales, gscale, h_out, static_cast<uint32_t*>(workspace),
+      mode, x, M, (int)K, ld, eps, codes, scales, gscale, h_out, sync,
       (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(), (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }

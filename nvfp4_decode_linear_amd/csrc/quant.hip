@@ -185,6 +185,19 @@ __device__ inline float block_sum_f32(float v, float* red) {
   return all;
 }
 
+// h = silu(g) * u for block j of a row (gate g = row[0, K), up u = row[K, 2K))
+__device__ inline void silu_mul_block(const uint16_t* row, int K, int j, float (&h)[16]) {
+  float u[16];
+  load16_bf16_f32(row + 16 * j, h);
+  load16_bf16_f32(row + K + 16 * j, u);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float g = h[i];
+    const float sig = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
+    h[i] = __fmul_rn(sig, u[i]);
+  }
+}
+
 // h of this thread's blocks of row `row` (blocks past the row are zero)
 template <int MODE, int BPT>
 __device__ inline void prep_row(const uint16_t* row, int K, float eps, float (&h)[BPT][16],
@@ -194,15 +207,7 @@ __device__ inline void prep_row(const uint16_t* row, int K, float eps, float (&h
   for (int r = 0; r < BPT; ++r) {
     const int j = min((int)threadIdx.x + r * kPrepThreads, nbr - 1);
     if constexpr (MODE == kPrepSilu) {
-      float u[16];
-      load16_bf16_f32(row + 16 * j, h[r]);
-      load16_bf16_f32(row + K + 16 * j, u);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float g = h[r][i];
-        const float sig = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
-        h[r][i] = __fmul_rn(sig, u[i]);
-      }
+      silu_mul_block(row, K, j, h[r]);
     } else {
       load16_bf16_f32(row + 16 * j, h[r]);
     }
@@ -292,6 +297,54 @@ __global__ __launch_bounds__(kPrepThreads) void prep_quant_kernel(
     const int j = (int)threadIdx.x + r * kPrepThreads;
     if (j < nbr) store_block(codes, scales, K, m, j, quantize_block_f32(h[r], sg));
   }
+}
+
+// SiLU * mul + quantization spread over workgroups of kActThreads threads:
+// thread t of workgroup w owns flat block i = w * kActThreads + t of the M x
+// K/16 blocks (row i / (K/16)), one block each, so the exp / divide work of a
+// row is shared by many CUs instead of one.  The tensor maximum is combined
+// across the grid as in act_quant_kernel (bounded poll; a workgroup that
+// gives up recomputes every block's h itself).  h and the codes are those of
+// prep_quant_kernel<kPrepSilu, *>: the same per-element operations and the
+// same exact maximum.
+__global__ __launch_bounds__(kActThreads) void silu_quant_spread_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, float* __restrict__ h_out,
+    uint32_t* sync, uint32_t spin_limit) {
+  __shared__ uint32_t red[kActThreads / kWave];
+  __shared__ uint32_t shared_amax;
+  const int nbr = K >> 4, nall = M * nbr;
+  const int i = (int)blockIdx.x * kActThreads + (int)threadIdx.x;
+  const int ic = min(i, nall - 1);
+  const int m = ic / nbr, j = ic - m * nbr;
+  float h[16];
+  silu_mul_block(x + (int64_t)m * ldx, K, j, h);
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) bmax = max(bmax, __float_as_uint(h[e]) & 0x7FFFFFFFu);
+  if (h_out && i < nall) {
+    float4* o = reinterpret_cast<float4*>(h_out + (int64_t)m * K + 16 * j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+  }
+  uint32_t amax = block_reduce_max(i < nall ? bmax : 0u, red);
+  if (gridDim.x > 1) {
+    amax = combine_amax(amax, sync, spin_limit, &shared_amax);
+    if (amax == kGaveUp) {                        // every block's h, this workgroup alone
+      uint32_t a2 = 0;
+      for (int b = threadIdx.x; b < nall; b += kActThreads) {
+        const int mm = b / nbr, jj = b - mm * nbr;
+        float hh[16];
+        silu_mul_block(x + (int64_t)mm * ldx, K, jj, hh);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a2 = max(a2, __float_as_uint(hh[e]) & 0x7FFFFFFFu);
+      }
+      amax = block_reduce_max(a2, red);
+    }
+  }
+  const float sg = tensor_scale(__uint_as_float(amax));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = sg;
+  if (i < nall) store_block(codes, scales, K, m, j, quantize_block_f32(h, __uint_as_float(bmax), sg));
 }
 
 // ---------------------------------------------------------------- weights
@@ -463,6 +516,12 @@ hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64
   hipLaunchKernelGGL((prep_quant_kernel<MODE, BPT>), g, b, 0, s, x, K, ldx, eps, codes, scales, \
                      gscale, h_out, sync, spin)
   const int bpt = prep_bpt(K);
+  if (mode == kPrepSilu && sync) {
+    const int groups = (M * (K >> 4) + kActThreads - 1) / kActThreads;   // <= 64
+    hipLaunchKernelGGL(silu_quant_spread_kernel, dim3(groups), dim3(kActThreads), 0, s, x, M, K,
+                       ldx, codes, scales, gscale, h_out, sync, spin);
+    return hipGetLastError();
+  }
   if (mode == kPrepRms) {
     if (bpt == 1) NVFP4_PREP(kPrepRms, 1);
     else NVFP4_PREP(kPrepRms, 2);

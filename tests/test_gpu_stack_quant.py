@@ -108,6 +108,30 @@ def test_fused_quantize_forced_fallback(nv, mode):
         assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
+@pytest.mark.parametrize("K", [512, 25600])
+def test_silu_mul_one_row_without_workspace(nv, K):
+    """At M = 1 the workspace is optional: without one a single workgroup
+    does the row, with one the blocks spread over workgroups.  Both must
+    give the same h, codes, scales and tensor scale."""
+    import ctypes
+    import torch
+    note(f"silu_mul quant M=1 K={K}, with and without workspace")
+    gu16 = activations_bf16(5, 7, 1, 2 * K, "student_t")
+    q1, h1 = _run(nv, "silu", gu16, K)
+    xd = to_dev_bf16(gu16)
+    q0 = nv.empty_act(1, K)
+    h0 = torch.empty((1, K), dtype=torch.float32, device="cuda")
+    st = nv._silu_mul_quantize_act(xd.data_ptr(), 1, K, xd.stride(0), q0.codes.data_ptr(),
+                                   q0.scales.data_ptr(), q0.gscale.data_ptr(), h0.data_ptr(),
+                                   None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    _sync()
+    assert np.array_equal(h0.cpu().numpy().view(np.uint32), h1.view(np.uint32))
+    for a, b in ((q0.codes, q1.codes), (q0.scales, q1.scales), (q0.gscale, q1.gscale)):
+        assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    _assert_quant_of(q0, h0.cpu().numpy())
+
+
 def test_fused_quantize_edges(nv):
     import torch
     note("rmsnorm quant zero row and constant row")
