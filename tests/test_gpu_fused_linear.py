@@ -46,7 +46,8 @@ def _both(nv, x, wq, out_dtype):
 
 
 SHAPES = [(256, 512, 1), (6144, 4096, 1), (4096, 4096, 2), (24576, 4096, 4), (4096, 12288, 1),
-          (4096, 4096, 8), (100, 1040, 3), (33, 16, 8), (5120, 25600, 1), (10240, 5120, 8)]
+          (4096, 4096, 8), (100, 1040, 3), (33, 16, 8), (5120, 25600, 1), (10240, 5120, 8),
+          (256, 5632, 8)]
 
 
 @pytest.fixture(params=[0, 1, 2], ids=["tiles_auto", "full_tiles", "half_tiles"])
@@ -113,7 +114,7 @@ def test_fused_strided_input_and_graph_replay(nv):
 
 
 RMS_SHAPES = [(6144, 4096, 1), (24576, 4096, 2), (10240, 5120, 1), (10240, 5120, 3),
-              (51200, 5120, 1), (10240, 5120, 8), (100, 1040, 3), (33, 16, 8)]
+              (51200, 5120, 1), (10240, 5120, 8), (100, 1040, 3), (33, 16, 8), (256, 5632, 8)]
 U32 = 2.0 ** -24
 
 
