@@ -9,8 +9,9 @@ prologue quantizes the activation).
 Weights are quantized once, then copied into enough distinct buffers
 (>= 1.2 GiB) that every step reads weights that are not resident in the
 256 MB Infinity Cache; step i uses copy i mod copies.  Each copy's step is
-captured into a HIP graph and a timed step is one graph replay, so the
-host's launch cost is not part of the measurement.  Inputs are seeded
+captured into a HIP graph and a timed step is one graph replay; a spin
+kernel holds the GPU while the host enqueues the timed replays, so the host's
+launch cost is not part of the measurement.  Inputs are seeded
 synthetic data with the shapes and distributions of that workload.
 
 Prints one JSON line with the step's whole-path algorithmic HBM bytes per
@@ -175,6 +176,25 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
         self.stream = torch.cuda.Stream()
+        self.cycles_per_ms = None
+
+    def lead(self, ms):
+        """Keep the GPU busy on the timing stream for about `ms` (torch's spin
+        kernel, calibrated once), so that the host has enqueued the timed
+        replays before the first of them starts: the events then bracket GPU
+        work only, with no gaps where the GPU waits for the host's launches."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            if self.cycles_per_ms is None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                probe = 200_000
+                e0.record(self.stream)
+                torch.cuda._sleep(probe)
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                self.cycles_per_ms = probe / max(e0.elapsed_time(e1), 1e-3)
+            torch.cuda._sleep(int(self.cycles_per_ms * ms))
 
     def capture(self, fn):
         torch = self.torch
@@ -197,6 +217,8 @@ class Timer:
                 graphs[i % len(graphs)].replay()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+        self.lead(1.0 + 0.1 * n)
+        with torch.cuda.stream(self.stream):
             e0.record(self.stream)
             for i in range(n):
                 graphs[i % len(graphs)].replay()
@@ -279,6 +301,7 @@ def main():
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    timer.lead(1.0 + 0.1 * args.steps)       # the host enqueues ahead of the GPU
     t0 = time.perf_counter()
     with torch.cuda.stream(timer.stream):
         t_start.record(timer.stream)
