@@ -277,8 +277,10 @@ nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void*
  * FP4 conversion at unit scale) against the rounding rule stated above
  * (nearest, ties to the even code, saturating at 6, sign bit from the input):
  * every finite binary32 pattern is encoded both ways, paired with its
- * negation.  result: 2 device uint64 (8-byte aligned), overwritten with
- * {patterns that differ, patterns checked}; expect {0, 2^32 - 2^24}.
+ * negation, both as a lone byte and written into bytes 1, 2 and 3 of a
+ * dword whose other bytes must stay.  result: 2 device uint64 (8-byte
+ * aligned), overwritten with {mismatches over those four forms, patterns
+ * checked}; expect {0, 2^32 - 2^24}.
  * Errors: NVFP4_ERR_INVALID_ARG for a null or misaligned result. */
 nvfp4_status nvfp4_selftest_e2m1(unsigned long long* result, void* stream);
 

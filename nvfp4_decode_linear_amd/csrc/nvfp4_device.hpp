@@ -70,6 +70,27 @@ __device__ inline uint32_t e2m1x2(float y0, float y1) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
 }
 
+// The same two codes written into byte SEL of `old`, its other bytes kept
+// (also checked on the device over every finite pattern).
+template <int SEL>
+__device__ inline uint32_t e2m1x2_into(uint32_t old, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, SEL);
+}
+
+// 16 values y(0..15) -> the block's two code dwords (element 2i in the low
+// nibble of byte i), one conversion per pair written straight into place.
+template <class Y>
+__device__ __forceinline__ void pack_e2m1_block(const Y& y, uint32_t& lo, uint32_t& hi) {
+  lo = e2m1x2_into<0>(0u, y(0), y(1));
+  lo = e2m1x2_into<1>(lo, y(2), y(3));
+  lo = e2m1x2_into<2>(lo, y(4), y(5));
+  lo = e2m1x2_into<3>(lo, y(6), y(7));
+  hi = e2m1x2_into<0>(0u, y(8), y(9));
+  hi = e2m1x2_into<1>(hi, y(10), y(11));
+  hi = e2m1x2_into<2>(hi, y(12), y(13));
+  hi = e2m1x2_into<3>(hi, y(14), y(15));
+}
+
 // One block of 16 bf16 values (32 bytes, 16-byte aligned) as 8 packed pairs.
 __device__ inline void load_block_bf16(const uint16_t* p, uint32_t (&v)[8]) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -115,15 +136,13 @@ __device__ inline BlockQ quantize_block_bf16(const uint32_t (&v)[8], uint32_t am
   const float r = (T == 0.0f) ? 0.0f : __fdiv_rn(1.0f, T);
   BlockQ q;
   q.scale = sb;
-  uint32_t w[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x0 = __uint_as_float(v[i] << 16);
-    const float x1 = __uint_as_float(v[i] & 0xFFFF0000u);
-    w[i >> 2] |= e2m1x2(__fmul_rn(x0, r), __fmul_rn(x1, r)) << (8 * (i & 3));
-  }
-  q.lo = w[0];
-  q.hi = w[1];
+  // element e: bf16 pair e / 2, low half for even e
+  pack_e2m1_block(
+      [&](int e) __attribute__((always_inline)) {
+        const uint32_t b = v[e >> 1];
+        return __fmul_rn(__uint_as_float((e & 1) ? (b & 0xFFFF0000u) : (b << 16)), r);
+      },
+      q.lo, q.hi);
   return q;
 }
 
@@ -140,12 +159,8 @@ __device__ inline BlockQ quantize_block_f32(const float (&x)[16], float a, float
   const float r = (T == 0.0f) ? 0.0f : __fdiv_rn(1.0f, T);
   BlockQ q;
   q.scale = sb;
-  uint32_t w[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i >> 2] |= e2m1x2(__fmul_rn(x[2 * i], r), __fmul_rn(x[2 * i + 1], r)) << (8 * (i & 3));
-  q.lo = w[0];
-  q.hi = w[1];
+  pack_e2m1_block([&](int e) __attribute__((always_inline)) { return __fmul_rn(x[e], r); },
+                  q.lo, q.hi);
   return q;
 }
 

@@ -454,6 +454,12 @@ __global__ __launch_bounds__(256) void e2m1_selftest_kernel(unsigned long long* 
     const float y = __uint_as_float(u), z = __uint_as_float(u ^ 0x80000000u);
     const uint32_t ref = f32_to_e2m1_rne_sat(y) | (f32_to_e2m1_rne_sat(z) << 4);
     bad += e2m1x2(y, z) != ref;
+    // the byte-select forms write the same byte into position 1, 2 or 3 of
+    // the old dword and keep its other bytes
+    const uint32_t old = 0xA5C3E10Fu ^ u;
+    bad += e2m1x2_into<1>(old, y, z) != ((old & ~0x0000FF00u) | (ref << 8));
+    bad += e2m1x2_into<2>(old, y, z) != ((old & ~0x00FF0000u) | (ref << 16));
+    bad += e2m1x2_into<3>(old, y, z) != ((old & ~0xFF000000u) | (ref << 24));
     ++seen;
   }
   atomicAdd(out, bad);
