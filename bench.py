@@ -100,6 +100,9 @@ def parse():
                     help="only the timed step and its roofline (no M sweep, 32B, stack)")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--stack-steps", type=int, default=1500)
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only the layer stack's decode step (no 8B step, no linear tables); "
+                         "prints its own JSON line (for kernel-trace runs of the stack)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only a 256 MiB device copy and a few GEMV launches of the "
                          "timed workload (for rocprofv3 counter runs), print nothing else")
@@ -282,6 +285,11 @@ def main():
         return
 
     timer = Timer(torch)
+    if args.stack_only:
+        res = bench_32b_and_stack(args, torch, nv, dev, timer, None)
+        print(json.dumps({"workload": "qwen3_32b_layer_stack", **res["stack_qwen3_32b"]}),
+              flush=True)
+        return
 
     # ---- the timed step: per projection act quant + linear, one graph per copy
     xqs = [nv.empty_act(M, L.K) for L in linears]
@@ -439,8 +447,8 @@ def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     xs = [to_dev(activations_bf16(4, li, 8, L.K, "student_t")) for li, L in enumerate(lins)]
-    lin32 = linear_table(lins, layers[:max(2, min(nl, int(np.ceil(1.2 * (1 << 30) / wbytes))))],
-                         (1, 4, 8), xs)
+    lin32 = None if args.stack_only else linear_table(
+        lins, layers[:max(2, min(nl, int(np.ceil(1.2 * (1 << 30) / wbytes))))], (1, 4, 8), xs)
 
     hidden, qkv_n, q_cols, ffn = 5120, 10240, 8192, 25600
     stack = {"layers": nl, "weight_bytes_per_step": int(nl * wbytes)}
