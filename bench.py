@@ -373,6 +373,19 @@ def main():
     tot_b = sum(step_linear_bytes(M, r["N"], r["K"]) for r in rows)
     tot_us = sum(r["us"] for r in rows)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
+    # the same kernel's roofline at every M of the sweep: mean algorithmic
+    # bytes per launch / mean launch time over the four projections, and the
+    # weakest projection
+    per_m = {}
+    for key, rs in per_linear.items():
+        mx = int(key[1:])
+        b = sum(step_linear_bytes(mx, r["N"], r["K"]) for r in rs)
+        us = sum(r["us"] for r in rs)
+        worst = min(rs, key=lambda r: r["frac"])
+        per_m[key] = {"achieved": round(b / (us * 1e-6) / 1e9, 1),
+                      "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "launch_us_mean": round(us / len(rs), 3),
+                      "worst": {"linear": worst["name"], "frac": worst["frac"]}}
     traffic, traffic_note = read_traffic(M)
     del wsets, base
 
@@ -409,7 +422,8 @@ def main():
                      "traffic": traffic, "kernel": GEMV_KERNEL,
                      "traffic_note": traffic_note,
                      "launch_us_mean": round(tot_us / len(rows), 3),
-                     "algorithmic_bytes_per_launch": round(tot_b / len(rows))},
+                     "algorithmic_bytes_per_launch": round(tot_b / len(rows)),
+                     "per_m": per_m},
         "per_linear": per_linear,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

@@ -186,6 +186,35 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
                                 uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Activation quantization with a caller-supplied tensor scale (a static,
+ * calibrated activation scale, as carried by checkpoints from an offline
+ * NVFP4 conversion: the "ReSET" GitHub README, "Quantize a model to NVFP4").
+ * The quantizer Q above with its first step replaced: gscale = *x_gscale
+ * (read on the device) instead of amax / 2688; every block then follows the
+ * same steps, so blocks whose sigma exceeds 448 saturate to scale 448 and
+ * codes +-6.
+ *   x_gscale  one device float, finite and > 0, not written; inputs with
+ *             a / (6 * x_gscale) beyond the binary32 range are outside the
+ *             contract (codes unspecified, never a crash)
+ *   other arguments as for nvfp4_quantize_act (no workspace: no tensor
+ *   maximum is combined across workgroups). */
+nvfp4_status nvfp4_quantize_act_static(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                       const float* x_gscale, uint8_t* x_codes, uint8_t* x_scales,
+                                       void* stream);
+
+/* nvfp4_quantize_linear with the static tensor scale of
+ * nvfp4_quantize_act_static: y = linear(Q_static(x)), bit-identical to
+ * nvfp4_quantize_act_static followed by nvfp4_linear with x_gscale as the
+ * activation tensor scale (x_codes and x_scales are written).  One kernel
+ * whenever nvfp4_quantize_linear would fuse (its prologue then takes no
+ * tensor maximum).  Workspace: nvfp4_quantize_linear_workspace_bytes. */
+nvfp4_status nvfp4_quantize_linear_static(int M, int64_t N, int64_t K, const uint16_t* x_bf16,
+                                          int64_t ldx, const float* x_gscale,
+                                          const uint8_t* w_codes, const uint8_t* w_scales,
+                                          const float* w_gscale, void* y, int out_dtype,
+                                          uint8_t* x_codes, uint8_t* x_scales, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Activation quantization and the decode linear in one call: the result is
  * bit-identical to nvfp4_quantize_act(x_bf16 -> x_codes, x_scales,
  * x_gscale) followed by nvfp4_linear on those outputs, which this call also
@@ -196,8 +225,9 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
  * otherwise (or with NVFP4_OPT_FUSE_QUANT = 0) the two launches run in
  * order.  Arguments as for nvfp4_quantize_act and nvfp4_linear; x_codes,
  * x_scales and x_gscale are outputs here.  The workspace must hold
- * nvfp4_quantize_linear_workspace_bytes(M, N, K) (the larger of the two
- * calls' needs; the same memory serves both). */
+ * nvfp4_quantize_linear_workspace_bytes(M, N, K): the larger of the two
+ * calls' needs and at least 16 bytes (the same memory serves both; 0 only
+ * for arguments the call rejects). */
 size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K);
 nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
                                    const uint8_t* w_codes, const uint8_t* w_scales,

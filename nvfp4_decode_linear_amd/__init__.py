@@ -65,6 +65,11 @@ _quantize_linear = _sig("nvfp4_quantize_linear", _c_int, _c_int, _c_i64, _c_i64,
                         _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp)
 _quantize_linear_workspace_bytes = _sig("nvfp4_quantize_linear_workspace_bytes", _c_size, _c_int,
                                         _c_i64, _c_i64)
+_quantize_act_static = _sig("nvfp4_quantize_act_static", _c_int, _vp, _c_int, _c_i64, _c_i64, _vp,
+                           _vp, _vp, _vp)
+_quantize_linear_static = _sig("nvfp4_quantize_linear_static", _c_int, _c_int, _c_i64, _c_i64, _vp,
+                               _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_size,
+                               _vp)
 _rmsnorm_quantize_linear = _sig("nvfp4_rmsnorm_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp,
                                 _c_i64, ctypes.c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
                                 _vp, _vp, _c_size, _vp)
@@ -213,6 +218,22 @@ def quantize_act(x, out: QuantAct | None = None, ws=None) -> QuantAct:
     _check(_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q.codes), _ptr(q.scales),
                          _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(x)), "nvfp4_quantize_act")
     return q
+
+
+def quantize_act_static(x, gscale, out: QuantAct | None = None) -> QuantAct:
+    """bf16 [M][K] -> canonical NVFP4 with a caller-supplied tensor scale
+    (float32 device tensor [1], e.g. a calibrated static activation scale);
+    the returned QuantAct's gscale is that tensor."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    if gscale.dtype != torch.float32 or gscale.numel() < 1:
+        raise ValueError("gscale must be a float32 device tensor")
+    M, K = x.shape
+    q = out if out is not None else empty_act(M, K, x.device)
+    _check(_quantize_act_static(_ptr(x), M, K, x.stride(0), _ptr(gscale), _ptr(q.codes),
+                                _ptr(q.scales), _stream(x)), "nvfp4_quantize_act_static")
+    return QuantAct(q.codes, q.scales, gscale, M, K)
 
 
 def _nullable(t):
@@ -373,6 +394,41 @@ def quantize_linear(x, wq: QuantWeight, out_dtype=None, out=None, xq: QuantAct |
                             _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(y)),
            "nvfp4_quantize_linear")
     return y, q
+
+
+def _out_args(x, wq, out_dtype, out):
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    if x.shape[1] != wq.K:
+        raise ValueError("K mismatch")
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    y = out if out is not None else torch.empty((x.shape[0], wq.N), dtype=out_dtype,
+                                                device=x.device)
+    return y, od
+
+
+def quantize_linear_static(x, gscale, wq: QuantWeight, out_dtype=None, out=None,
+                           xq: QuantAct | None = None, ws=None):
+    """quantize_linear with a caller-supplied activation tensor scale
+    (float32 device tensor [1]); returns (y, xq) with xq.gscale = gscale."""
+    torch = _torch()
+    if gscale.dtype != torch.float32 or gscale.numel() < 1:
+        raise ValueError("gscale must be a float32 device tensor")
+    y, od = _out_args(x, wq, out_dtype, out)
+    M, K = x.shape
+    q = xq if xq is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(M, wq.N, K, x.device)
+    _check(_quantize_linear_static(M, wq.N, K, _ptr(x), x.stride(0), _ptr(gscale),
+                                   _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), od,
+                                   _ptr(q.codes), _ptr(q.scales), _ptr(ws), ws.numel(),
+                                   _stream(y)), "nvfp4_quantize_linear_static")
+    return y, QuantAct(q.codes, q.scales, gscale, M, K)
 
 
 def rmsnorm_quantize_linear(x, wq: QuantWeight, eps=1e-6, out_dtype=None, out=None,

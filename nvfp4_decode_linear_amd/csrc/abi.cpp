@@ -1,8 +1,9 @@
 // C ABI of the NVFP4 decode-linear library (include/nvfp4.h): argument
 // validation on the host before any HIP call, runtime knobs, launch plans,
-// and dispatch to the gfx950 kernels.  The runtime knobs follow the README's
-// "nvfp4r.configure(gemv_max_m=2)" / "nvfp4r.status()" example ("ReSET"
-// GitHub README, "Run benchmarks").
+// and dispatch to the gfx950 kernels.  The runtime knobs play the part of the
+// kernel package's configure / status calls in the Python wiring example of
+// the "ReSET" GitHub README, section "Run benchmarks" (a threshold on M below
+// which the CUDA-core GEMV runs, and a way to read the settings back).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -363,30 +364,43 @@ nvfp4_status nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, int64_
 }
 
 size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxM || !valid_nk(N, K) ||
+      N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
+      (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks)
+    return 0;
+  // At least the sync record: when the call is not fused, its quantizer (the
+  // plain one, or the RMS-norm one that needs the record whenever M > 1)
+  // runs as its own launch on this workspace.
+  size_t need = nvfp4::kActSyncBytes;
   const size_t lin = nvfp4_linear_workspace_bytes(M, N, K);
   const size_t act = nvfp4_act_workspace_bytes(M, K);
-  return lin > act ? lin : act;
+  if (lin > need) need = lin;
+  if (act > need) need = act;
+  return need;
 }
 
 namespace {
 
-// nvfp4_quantize_linear (rms = 0) and nvfp4_rmsnorm_quantize_linear (rms = 1)
-nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, int M, int64_t N, int64_t K,
-                                  const uint16_t* x_bf16, int64_t ldx, const uint8_t* w_codes,
-                                  const uint8_t* w_scales, const float* w_gscale, void* y,
-                                  int out_dtype, uint8_t* x_codes, uint8_t* x_scales,
-                                  float* x_gscale, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+// nvfp4_quantize_linear (rms = 0), nvfp4_rmsnorm_quantize_linear (rms = 1)
+// and, with sg_static set, nvfp4_quantize_linear_static (x_gscale unused)
+nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, const float* sg_static, int M,
+                                  int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
+                                  const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
+                                  uint8_t* x_scales, float* x_gscale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
   if (M < 1 || !valid_nk(N, K) || N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
       (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks || ldx < K || ldx % 8 != 0)
     return NVFP4_ERR_INVALID_ARG;
   if (rms && (K > nvfp4::kPrepMaxK || !(eps >= 0.0f) || !std::isfinite(eps)))
     return NVFP4_ERR_INVALID_ARG;
-  if (!x_bf16 || !w_codes || !w_scales || !w_gscale || !y || !x_codes || !x_scales || !x_gscale)
+  if (!x_bf16 || !w_codes || !w_scales || !w_gscale || !y || !x_codes || !x_scales ||
+      !(sg_static ? sg_static : x_gscale))
     return NVFP4_ERR_INVALID_ARG;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_INVALID_ARG;
-  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
+  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) ||
+      !aligned(sg_static ? sg_static : x_gscale, 4) ||
       !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
       !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2) || (h_out && !aligned(h_out, 16)))
     return NVFP4_ERR_INVALID_ARG;
@@ -401,13 +415,15 @@ nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, int M, int64
   if (!fused) {
     // two launches: the (RMS norm +) activation quantizer, then the linear
     const nvfp4_status st =
-        rms ? nvfp4_rmsnorm_quantize_act(x_bf16, M, K, ldx, eps, x_codes, x_scales, x_gscale,
-                                         h_out, workspace, workspace_bytes, stream)
-            : nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale, workspace,
-                                 workspace_bytes, stream);
+        sg_static ? nvfp4_quantize_act_static(x_bf16, M, K, ldx, sg_static, x_codes, x_scales,
+                                              stream)
+        : rms     ? nvfp4_rmsnorm_quantize_act(x_bf16, M, K, ldx, eps, x_codes, x_scales,
+                                               x_gscale, h_out, workspace, workspace_bytes, stream)
+                  : nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale, workspace,
+                                       workspace_bytes, stream);
     if (st != NVFP4_OK) return st;
-    return nvfp4_linear(M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y,
-                        out_dtype, workspace, workspace_bytes, stream);
+    return nvfp4_linear(M, N, K, x_codes, x_scales, sg_static ? sg_static : x_gscale, w_codes,
+                        w_scales, w_gscale, y, out_dtype, workspace, workspace_bytes, stream);
   }
   if (p.ws_bytes > 0) {
     if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARG;
@@ -416,19 +432,49 @@ nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, int M, int64
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
   const hipError_t e = nvfp4::launch_gemv_stream(
       p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y, out_dtype,
-      workspace, (hipStream_t)stream, x_bf16, ldx, x_codes, x_scales, x_gscale, rms, eps, h_out);
+      workspace, (hipStream_t)stream, x_bf16, ldx, x_codes, x_scales, x_gscale, rms, eps, h_out,
+      sg_static);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
 }  // namespace
+
+nvfp4_status nvfp4_quantize_act_static(const uint16_t* x_bf16, int M, int64_t K, int64_t ldx,
+                                       const float* x_gscale, uint8_t* x_codes, uint8_t* x_scales,
+                                       void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (!x_bf16 || !x_codes || !x_scales || !x_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || K < 16 || K % 16 != 0 || (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks ||
+      ldx < K || ldx % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4))
+    return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_quantize_act(
+      x_bf16, M, (int)K, ldx, x_codes, x_scales, nullptr, nullptr, 0, (hipStream_t)stream,
+      x_gscale);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_quantize_linear_static(int M, int64_t N, int64_t K, const uint16_t* x_bf16,
+                                          int64_t ldx, const float* x_gscale,
+                                          const uint8_t* w_codes, const uint8_t* w_scales,
+                                          const float* w_gscale, void* y, int out_dtype,
+                                          uint8_t* x_codes, uint8_t* x_scales, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (!x_gscale) return M > kMaxM ? NVFP4_ERR_UNSUPPORTED : NVFP4_ERR_INVALID_ARG;
+  return quantize_linear_impl(0, 0.0f, nullptr, x_gscale, M, N, K, x_bf16, ldx, w_codes, w_scales,
+                              w_gscale, y, out_dtype, x_codes, x_scales, nullptr, workspace,
+                              workspace_bytes, stream);
+}
 
 nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ldx,
                                    const uint8_t* w_codes, const uint8_t* w_scales,
                                    const float* w_gscale, void* y, int out_dtype, uint8_t* x_codes,
                                    uint8_t* x_scales, float* x_gscale, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  return quantize_linear_impl(0, 0.0f, nullptr, M, N, K, x_bf16, ldx, w_codes, w_scales, w_gscale,
-                              y, out_dtype, x_codes, x_scales, x_gscale, workspace,
+  return quantize_linear_impl(0, 0.0f, nullptr, nullptr, M, N, K, x_bf16, ldx, w_codes, w_scales,
+                              w_gscale, y, out_dtype, x_codes, x_scales, x_gscale, workspace,
                               workspace_bytes, stream);
 }
 
@@ -439,9 +485,9 @@ nvfp4_status nvfp4_rmsnorm_quantize_linear(int M, int64_t N, int64_t K, const ui
                                            uint8_t* x_scales, float* x_gscale, float* h_out,
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
-  return quantize_linear_impl(1, eps, h_out, M, N, K, x_bf16, ldx, w_codes, w_scales, w_gscale, y,
-                              out_dtype, x_codes, x_scales, x_gscale, workspace, workspace_bytes,
-                              stream);
+  return quantize_linear_impl(1, eps, h_out, nullptr, M, N, K, x_bf16, ldx, w_codes, w_scales,
+                              w_gscale, y, out_dtype, x_codes, x_scales, x_gscale, workspace,
+                              workspace_bytes, stream);
 }
 
 namespace {

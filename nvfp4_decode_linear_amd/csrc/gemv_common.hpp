@@ -49,6 +49,8 @@ struct GemvArgs {
   int rms;       // nonzero: RMS-normalise each row (epsilon eps) before quantizing
   float eps;
   float* ho;     // optional binary32 h [M][K] (workgroup 0)
+  const float* sgs;  // a caller-supplied (static) activation tensor scale: the
+                     // prologue then takes no tensor maximum and writes no og
 };
 
 __device__ inline u32x4 load_codes(const uint8_t* p, bool nt) {

@@ -9,8 +9,9 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
                               const uint8_t* ws, const float* wg, void* y, int out_bf16,
                               void* workspace, hipStream_t s, const uint16_t* xb, int64_t ldx,
                               uint8_t* oc, uint8_t* os, float* og, int rms, float eps,
-                              float* ho) {
+                              float* ho, const float* sgs) {
   GemvArgs a = {};
+  a.sgs = sgs;
   a.rms = rms;
   a.eps = eps;
   a.ho = ho;

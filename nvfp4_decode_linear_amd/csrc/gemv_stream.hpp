@@ -353,12 +353,17 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       bmx[r] = b;
       amax = max(amax, i < nreal ? b : 0u);
     }
-    amax = wave_max_u32(amax);
-    if (lane == 0) wred[wave] = amax;
-    __syncthreads();
-    amax = 0;
-    for (int w = 0; w < NW; ++w) amax = max(amax, wred[w]);
-    const float sg = tensor_scale(QA == 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
+    float sg;
+    if (a.sgs) {                                      // uniform: a static tensor scale
+      sg = *a.sgs;
+    } else {
+      amax = wave_max_u32(amax);
+      if (lane == 0) wred[wave] = amax;
+      __syncthreads();
+      amax = 0;
+      for (int w = 0; w < NW; ++w) amax = max(amax, wred[w]);
+      sg = tensor_scale(QA == 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
+    }
     g = __fmul_rn(sg, a.wg[0]);
     const bool out = blockIdx.x == 0;
 #pragma unroll
@@ -387,7 +392,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         }
       }
     }
-    if (out && threadIdx.x == 0) *a.og = sg;
+    if (out && threadIdx.x == 0 && !a.sgs) *a.og = sg;
     const int npad = kc * 4 - kb_row;                 // zero blocks up to the padded K
     for (int i = threadIdx.x; i < M * npad; i += T) {
       const int m = i / npad;

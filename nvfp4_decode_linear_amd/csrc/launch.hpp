@@ -60,9 +60,11 @@ constexpr int64_t kActMaxBlocks = 256 * 256 * 4;
 constexpr size_t kActSyncBytes = 16;
 ActPlan act_plan(int M, int64_t K);
 
+// sg_static: quantize with this device tensor scale instead of the tensor's
+// own (gscale is then not written and sync not used).
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
                                uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
-                               hipStream_t s);
+                               hipStream_t s, const float* sg_static = nullptr);
 
 // Fused stack quantizers (mode 0: RMS norm, 1: SiLU * mul), one workgroup
 // per row of up to 2 * 1024 blocks, K <= kPrepMaxK.
@@ -94,7 +96,7 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               const uint16_t* xb = nullptr, int64_t ldx = 0,
                               uint8_t* oc = nullptr, uint8_t* os = nullptr,
                               float* og = nullptr, int rms = 0, float eps = 0.0f,
-                              float* ho = nullptr);
+                              float* ho = nullptr, const float* sgs = nullptr);
 
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
 // (4 bf16 blocks per thread).

@@ -110,11 +110,14 @@ __device__ uint32_t combine_amax(uint32_t amax, uint32_t* sync, uint32_t spin_li
   return *shared_slot;
 }
 
+// sg_static: a caller-supplied tensor scale (a calibrated, static activation
+// scale); then no tensor maximum is taken, every workgroup quantizes its own
+// blocks alone, and gscale is not written.
 template <int BPT>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ gscale, uint32_t* sync,
-    uint32_t spin_limit) {
+    uint32_t spin_limit, const float* __restrict__ sg_static) {
   __shared__ uint32_t red[kActThreads / kWave];
   __shared__ uint32_t shared_amax;
   const int nbr = K >> 4;
@@ -128,18 +131,21 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const int m = b / nbr, j = b - m * nbr;
     load_block_bf16(x + (int64_t)m * ldx + 16 * j, v[r]);
   }
-  uint32_t amax = 0;
+  float sg;
+  if (sg_static) {                              // uniform: no tensor maximum
+    sg = *sg_static;
+  } else {
+    uint32_t amax = 0;
 #pragma unroll
-  for (int r = 0; r < BPT; ++r) amax = max(amax, absmax_bits(v[r]));
-  amax = block_reduce_max(amax, red);
-
-  if (gridDim.x > 1) {
-    amax = combine_amax(amax, sync, spin_limit, &shared_amax);
-    if (amax == kGaveUp) amax = tensor_amax_bits(x, M, K, ldx, red);
+    for (int r = 0; r < BPT; ++r) amax = max(amax, absmax_bits(v[r]));
+    amax = block_reduce_max(amax, red);
+    if (gridDim.x > 1) {
+      amax = combine_amax(amax, sync, spin_limit, &shared_amax);
+      if (amax == kGaveUp) amax = tensor_amax_bits(x, M, K, ldx, red);
+    }
+    sg = tensor_scale(bf16_to_f32(amax));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = sg;
   }
-
-  const float sg = tensor_scale(bf16_to_f32(amax));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = sg;
 #pragma unroll
   for (int r = 0; r < BPT; ++r) {
     const int b = b0 + r * stride;
@@ -489,21 +495,21 @@ ActPlan act_plan(int M, int64_t K) {
 
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uint8_t* codes,
                                uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
-                               hipStream_t s) {
+                               hipStream_t s, const float* sg_static) {
   const ActPlan p = act_plan(M, K);
   const uint32_t spin = spin_limit ? spin_limit : kActDefaultSpin;
   switch (p.bpt) {
     case 1:
       hipLaunchKernelGGL(act_quant_kernel<1>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
-                         ldx, codes, scales, gscale, sync, spin);
+                         ldx, codes, scales, gscale, sync, spin, sg_static);
       break;
     case 2:
       hipLaunchKernelGGL(act_quant_kernel<2>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
-                         ldx, codes, scales, gscale, sync, spin);
+                         ldx, codes, scales, gscale, sync, spin, sg_static);
       break;
     case 4:
       hipLaunchKernelGGL(act_quant_kernel<4>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, K,
-                         ldx, codes, scales, gscale, sync, spin);
+                         ldx, codes, scales, gscale, sync, spin, sg_static);
       break;
     default:
       return hipErrorInvalidValue;

@@ -262,5 +262,10 @@ def linear_exact(xq: NVFP4Tensor, wq: NVFP4Tensor):
 
 
 def tolerance_bound(xq: NVFP4Tensor, wq: NVFP4Tensor, rel: float = 1e-3) -> np.ndarray:
-    """Per-element bound rel * sum_k |x_hat[m,k] * w_hat[n,k]| (float64)."""
+    """Per-element bound rel * sum_k |x_hat[m,k] * w_hat[n,k]| (float64).
+
+    Pinned by exact rational sums built from the spec value tables under
+    tests/golden/ with distinct block and tensor scales (rel = 1 and the
+    default rel = 1e-3), and by a cancelling dot whose output is 0 while the
+    bound is not (tests/test_oracle_dot.py)."""
     return rel * (np.abs(dequantize(xq)) @ np.abs(dequantize(wq)).T)

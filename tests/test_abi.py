@@ -262,4 +262,29 @@ def test_quantize_linear_argument_errors(lib, no_gpu):
     lib.nvfp4_quantize_linear_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
     lib.nvfp4_quantize_linear_workspace_bytes.restype = ctypes.c_size_t
     assert lib.nvfp4_quantize_linear_workspace_bytes(8, 24576, 4096) == 16   # act sync record
-    assert lib.nvfp4_quantize_linear_workspace_bytes(1, 24576, 4096) == 0
+    # at least the sync record for every valid shape: the unfused fallback of
+    # the RMS-norm variant needs it whenever M > 1
+    assert lib.nvfp4_quantize_linear_workspace_bytes(1, 24576, 4096) == 16
+    assert lib.nvfp4_quantize_linear_workspace_bytes(2, 4096, 4096) == 16
+    assert lib.nvfp4_quantize_linear_workspace_bytes(9, 4096, 4096) == 0
+    assert lib.nvfp4_quantize_linear_workspace_bytes(1, 4096, 24) == 0
+
+
+def test_static_scale_argument_errors(lib, no_gpu):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    a = lib.nvfp4_quantize_act_static
+    a.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp]
+    assert a(FAKE, 9, 512, 512, FAKE, FAKE, FAKE, None) == 2
+    assert a(FAKE, 1, 520, 520, FAKE, FAKE, FAKE, None) == 1          # K % 16
+    assert a(FAKE, 1, 512, 500, FAKE, FAKE, FAKE, None) == 1          # ldx < K
+    assert a(FAKE, 1, 512, 512, None, FAKE, FAKE, None) == 1          # no scale
+    assert a(FAKE, 1, 512, 512, ctypes.c_void_p(0x1002), FAKE, FAKE, None) == 1   # alignment
+    assert a(FAKE, 8, 25600, 25600, FAKE, FAKE, FAKE, None) == 3      # no workspace needed
+    f = lib.nvfp4_quantize_linear_static
+    f.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                  ctypes.c_size_t, vp]
+    ok = (FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert f(9, 256, 512, FAKE, 512, FAKE, *ok) == 2
+    assert f(1, 256, 512, FAKE, 512, None, *ok) == 1                  # no scale
+    assert f(1, 256, 512, FAKE, 500, FAKE, *ok) == 1                  # ldx < K
+    assert f(1, 256, 512, FAKE, 512, FAKE, *ok) == 3                  # no device

@@ -257,15 +257,30 @@ def test_weight_quant_ragged_full_and_padding(nv, N, K):
 
 @pytest.mark.parametrize("lin", range(4))
 @pytest.mark.parametrize("family", ["8b", "32b"])
-def test_weight_quant_model_shapes_sampled(nv, family, lin):
+def test_weight_quant_model_shapes_all_rows(nv, family, lin):
+    """Every row of every Qwen3-8B and Qwen3-32B projection weight, bit for
+    bit: the oracle quantizes the whole weight (in chunks of rows, with the
+    tensor scale of the whole weight) and every code and scale byte of the
+    GPU's tiled result, unpacked, must match."""
     cfg, shapes = (2, QWEN3_8B) if family == "8b" else (4, QWEN3_32B)
     L = shapes[lin]
-    note(f"weight quant {family} {L.name} N={L.N} K={L.K} (sampled rows)")
+    note(f"weight quant {family} {L.name} N={L.N} K={L.K} (all rows)")
     w16 = weights_bf16(cfg, lin, L.N, L.K)
-    rng = np.random.default_rng(lin)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(L.N - 64, L.N),
-                                     rng.choice(L.N, 192, replace=False)]))
-    _check_weight(nv, w16, rows)
+    wq = nv.quantize_weight(to_dev_bf16(w16))
+    c, s = nv.unpack_weight(wq)
+    _sync()
+    gc, gsc = c.cpu().numpy(), s.cpu().numpy()
+    del c, s
+    wf = bf16_to_f32(w16)
+    _, sg = oracle.global_scale(wf)
+    assert _gs_bits(wq.gscale) == np.asarray(sg, np.float32).view(np.uint32)
+    step = 2048
+    for r0 in range(0, L.N, step):
+        rc, rs = oracle.quantize_blocks(wf[r0:r0 + step], sg)
+        bad = np.nonzero(gsc[r0:r0 + step] != rs)
+        assert bad[0].size == 0, f"scale mismatch rows {r0 + bad[0][:4]} blocks {bad[1][:4]}"
+        bad = np.nonzero(gc[r0:r0 + step] != rc)
+        assert bad[0].size == 0, f"code mismatch rows {r0 + bad[0][:4]} bytes {bad[1][:4]}"
 
 
 def test_weight_every_scale_byte(nv):

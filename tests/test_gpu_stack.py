@@ -3,7 +3,9 @@ against the same step issued op by op through the C ABI (bit-identical: the
 same kernels in the same order), replays with fresh inputs and eager work in
 between, and, teacher-forced on the first and last layer, every op of the
 step against the oracle (the quantizers bit-exact given their input, the
-linears within the tolerance bound)."""
+linears within the tolerance bound).  Toy widths check every output; the
+Qwen3-32B decoder shapes (two layers at M = 1 and M = 8) check every op of
+both layers, the linears on sampled output columns."""
 
 import numpy as np
 import pytest
@@ -19,6 +21,18 @@ CONFIGS = [  # M, hidden, qkv_n, q_cols, ffn, layers
     (2, 512, 768, 512, 1024, 3),
     (1, 256, 384, 256, 512, 2),
     (8, 512, 640, 384, 768, 2),
+    # M = 8 at the 32B hidden width with a small FFN: 8 x 5120 / 16 = 2560
+    # activation blocks, past the fused prologue, so the RMS norm and the q
+    # slice are quantized by their own kernels on the shared workspace
+    (8, 5120, 1024, 1024, 512, 2),
+]
+# The Qwen3-32B decoder shapes (hidden 5120, QKV 10240, q slice 8192, FFN
+# 25600) of the 64-layer decode step that the "ReSET" GitHub README's demo
+# caption times (batch 1, graph replay, 1,500 tokens); two layers, at one row
+# and at eight.
+CONFIGS_32B = [
+    (1, 5120, 10240, 8192, 25600, 2),
+    (8, 5120, 10240, 8192, 25600, 2),
 ]
 
 
@@ -86,18 +100,38 @@ def _check_quant(a, h32):
                                                                    np.float32).view(np.uint32)
 
 
-def _check_linear(y_bf16, a, w16):
-    ow = oracle.quantize(bf16_to_f32(w16))
+def _sample_rows(N, seed, n=256):
+    """Output columns checked at the large shapes: both ends of the row range
+    (the first and the ragged last tiles) and a random sample."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(min(N, 48)), np.arange(max(0, N - 48), N),
+                                     rng.choice(N, min(N, n), replace=False)]))
+
+
+def _check_linear(y_bf16, a, w16, cols=None):
+    """The linear's bf16 output against the oracle on the GPU's quantized
+    activation (itself checked against the oracle quantizer before); the
+    oracle quantizes the weight rows (all, or the sampled `cols`) itself,
+    with the tensor scale of the whole weight."""
+    wf = bf16_to_f32(w16)
+    if cols is None:
+        ow = oracle.quantize(wf)
+    else:
+        _, sg = oracle.global_scale(wf)
+        wc, ws = oracle.quantize_blocks(wf[cols], sg)
+        ow = oracle.NVFP4Tensor(wc, ws, np.asarray(sg, np.float32))
     ox = _oracle_act(a)
     ref = oracle.linear_ref(ox, ow)
     bound = oracle.tolerance_bound(ox, ow) + 0.5 * np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
     got = y_bf16.float().cpu().numpy().astype(np.float64)
+    if cols is not None:
+        got = got[:, cols]
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
 
 
-@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("cfg", CONFIGS + CONFIGS_32B)
 def test_stack_graph_matches_op_by_op(nv, cfg):
     import torch
     M, hidden, qkv_n, q_cols, ffn, layers = cfg
@@ -131,15 +165,17 @@ def test_stack_graph_matches_op_by_op(nv, cfg):
         st.close()
 
 
-@pytest.mark.parametrize("cfg", CONFIGS[:2])
+@pytest.mark.parametrize("cfg", CONFIGS + CONFIGS_32B)
 def test_stack_ops_teacher_forced_vs_oracle(nv, cfg):
     import torch
     M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    big = cfg in CONFIGS_32B
+    note(f"stack teacher-forced cfg={cfg}: weights")
     src, wq = _weights(nv, cfg)
     x = to_dev_bf16(activations_bf16(7, 5, M, hidden, "outlier"))
     _, ops = _eager(nv, cfg, wq, x, trace=True)
     _sync()
-    for l in sorted({0, layers - 1}):
+    for l in range(layers) if big else sorted({0, layers - 1}):
         note(f"stack teacher-forced layer {l} cfg={cfg}")
         t = ops[l]
         w16 = src[l]
@@ -148,19 +184,20 @@ def test_stack_ops_teacher_forced_vs_oracle(nv, cfg):
         ref = oracle.rms_norm_rows(xin.astype(np.float64))
         assert np.all(np.abs(h1 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
         _check_quant(t["a1"], h1)
-        _check_linear(t["qkv"], t["a1"], w16[0])
+        cs = (lambda N, j: _sample_rows(N, 100 * l + j)) if big else (lambda N, j: None)
+        _check_linear(t["qkv"], t["a1"], w16[0], cs(qkv_n, 0))
         qs = bf16_to_f32(t["qkv"].cpu().view(torch.int16).numpy().view(np.uint16))[:, :q_cols]
         _check_quant(t["a2"], qs)
-        _check_linear(t["o"], t["a2"], w16[1])
+        _check_linear(t["o"], t["a2"], w16[1], cs(hidden, 1))
         oin = bf16_to_f32(t["o"].cpu().view(torch.int16).numpy().view(np.uint16))
         h3 = t["h3"].cpu().numpy()
         ref = oracle.rms_norm_rows(oin.astype(np.float64))
         assert np.all(np.abs(h3 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
         _check_quant(t["a3"], h3)
-        _check_linear(t["gu"], t["a3"], w16[2])
+        _check_linear(t["gu"], t["a3"], w16[2], cs(2 * ffn, 2))
         gin = bf16_to_f32(t["gu"].cpu().view(torch.int16).numpy().view(np.uint16))
         h4 = t["h4"].cpu().numpy()
         ref = oracle.silu_mul(gin.astype(np.float64))
         assert np.all(np.abs(h4 - ref) <= 16 * U32 * np.abs(ref) + 1e-30)
         _check_quant(t["a4"], h4)
-        _check_linear(t["dn"], t["a4"], w16[3])
+        _check_linear(t["dn"], t["a4"], w16[3], cs(hidden, 3))
