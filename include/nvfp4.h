@@ -329,6 +329,32 @@ nvfp4_status nvfp4_linear(int M, int64_t N, int64_t K, const uint8_t* x_codes,
                           const uint8_t* w_scales, const float* w_gscale, void* y, int out_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * nvfp4_quantize_linear (same arguments, same kernels, bit-identical
+ * results) without the workspace arguments.  The workspace lives in a
+ * library-owned device array of NVFP4_NOALLOC_SCRATCH_BYTES, one per device,
+ * held until the process ends; the call allocates nothing.
+ *   - Shapes whose nvfp4_quantize_linear_workspace_bytes exceeds
+ *     NVFP4_NOALLOC_SCRATCH_BYTES return NVFP4_ERR_WORKSPACE, before any
+ *     HIP call.  The default plans of all shapes with N <= 65536, K <= 32768
+ *     and M * K <= 204800 (e.g. K <= 25600 at M = 8) fit; larger
+ *     activations run the split-K kernel, whose partial sums can exceed it,
+ *     and so can forcing many K slices with NVFP4_OPT_SPLIT_K.
+ *   - The first call on a device takes the array's device address and
+ *     zeroes the array with a fill kernel on `stream`; make that first call
+ *     outside stream capture.  Later calls need no clearing (the counters
+ *     and the sync record in it return to zero at the end of every call).
+ *   - All calls on one device share the one array: calls that can overlap
+ *     on one device (different streams without ordering) race and give
+ *     wrong results.  Order them on one stream. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+nvfp4_status nvfp4_quantize_linear_noalloc(int M, int64_t N, int64_t K, const uint16_t* x_bf16,
+                                           int64_t ldx, const uint8_t* w_codes,
+                                           const uint8_t* w_scales, const float* w_gscale,
+                                           void* y, int out_dtype, uint8_t* x_codes,
+                                           uint8_t* x_scales, float* x_gscale, void* stream);
+
 /* ------------------------------------------------------------------------
  * Layer stack: one decode step of an L-layer stack of NVFP4 linears at M
  * rows, captured once into a HIP graph and replayed (the end-to-end figure

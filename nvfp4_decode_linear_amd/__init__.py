@@ -70,6 +70,8 @@ _quantize_act_static = _sig("nvfp4_quantize_act_static", _c_int, _vp, _c_int, _c
 _quantize_linear_static = _sig("nvfp4_quantize_linear_static", _c_int, _c_int, _c_i64, _c_i64, _vp,
                                _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_size,
                                _vp)
+_quantize_linear_noalloc = _sig("nvfp4_quantize_linear_noalloc", _c_int, _c_int, _c_i64, _c_i64,
+                                _vp, _c_i64, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp)
 _rmsnorm_quantize_linear = _sig("nvfp4_rmsnorm_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp,
                                 _c_i64, ctypes.c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
                                 _vp, _vp, _c_size, _vp)
@@ -429,6 +431,19 @@ def quantize_linear_static(x, gscale, wq: QuantWeight, out_dtype=None, out=None,
                                    _ptr(q.codes), _ptr(q.scales), _ptr(ws), ws.numel(),
                                    _stream(y)), "nvfp4_quantize_linear_static")
     return y, QuantAct(q.codes, q.scales, gscale, M, K)
+
+
+def quantize_linear_noalloc(x, wq: QuantWeight, out, xq: QuantAct):
+    """quantize_linear on the library's own scratch workspace (no workspace
+    argument, nothing allocated by the call): the caller passes the output
+    and the quantized-activation buffers."""
+    y, od = _out_args(x, wq, None, out)
+    M, K = x.shape
+    _check(_quantize_linear_noalloc(M, wq.N, K, _ptr(x), x.stride(0), _ptr(wq.codes),
+                                    _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), od,
+                                    _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.gscale),
+                                    _stream(y)), "nvfp4_quantize_linear_noalloc")
+    return y, xq
 
 
 def rmsnorm_quantize_linear(x, wq: QuantWeight, eps=1e-6, out_dtype=None, out=None,

@@ -288,3 +288,36 @@ def test_static_scale_argument_errors(lib, no_gpu):
     assert f(1, 256, 512, FAKE, 512, None, *ok) == 1                  # no scale
     assert f(1, 256, 512, FAKE, 500, FAKE, *ok) == 1                  # ldx < K
     assert f(1, 256, 512, FAKE, 512, FAKE, *ok) == 3                  # no device
+
+
+def test_noalloc_argument_errors_and_scratch_size(lib, no_gpu):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.nvfp4_quantize_linear_noalloc
+    f.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    ok = (FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None)
+    assert f(9, 256, 512, FAKE, 512, *ok) == 2
+    assert f(1, 256, 520, FAKE, 520, *ok) == 1
+    assert f(1, 256, 512, FAKE, 500, *ok) == 1                        # ldx < K
+    assert f(1, 256, 512, None, 512, *ok) == 1
+    bad = list(ok)
+    bad[4] = 7
+    assert f(1, 256, 512, FAKE, 512, *bad) == 1                       # output dtype
+    # the library's scratch: 4 MiB (the header's NVFP4_NOALLOC_SCRATCH_BYTES)
+    hdr = open(HEADER).read()
+    assert "#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)" in hdr
+    cap = 4 << 20
+    q = lib.nvfp4_quantize_linear_workspace_bytes
+    q.argtypes = [ctypes.c_int, i64, i64]
+    q.restype = ctypes.c_size_t
+    for M in range(1, 9):
+        for N in (1, 31, 256, 1024, 2016, 4096, 5120, 6144, 10240, 24576, 51200, 65536):
+            for K in (16, 512, 4096, 5120, 8192, 12288, 25600, 32768):
+                if M * K <= 204800:
+                    assert 0 < q(M, N, K) <= cap, (M, N, K)
+    # forcing many K slices exceeds the scratch: rejected before any HIP call
+    assert lib.nvfp4_set_option(1, 64) == 0
+    try:
+        assert q(8, 65536, 32768) > cap
+        assert f(8, 65536, 32768, FAKE, 32768, *ok) == 4
+    finally:
+        assert lib.nvfp4_set_option(1, 0) == 0
