@@ -94,7 +94,6 @@ void finish_workspace(GemvPlan& p, int M) {
 }
 
 constexpr int kStreamGrid = 256;   // one streaming workgroup per CU
-constexpr int kStreamGridMany = 192;  // M = 1 with more items than CUs (see make_plan)
 
 // K slices per row tile for the streaming kernels: with fewer than 64 row
 // tiles, enough (tile, slice) items to occupy more of the 256 workgroups,
@@ -149,36 +148,37 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     const int64_t force_grid = g_opts[NVFP4_OPT_GRID].load();
     int cpw, waves, cps, splits, grid;
     int64_t items, per_wg;
-    int grid_cap = kStreamGrid;
+    // The grid: the fewest rounds of at most 256 workgroups (one per CU), then
+    // as few workgroups as keep that number of rounds, so every workgroup
+    // streams the same number of items.  A partial last round leaves the
+    // memory system to the workgroups still running, which cannot use all
+    // of it (1600 row tiles of the 32B gate_up projection: 229 workgroups of
+    // 7 items measured 27.8 us at M = 1 and 36.6 us at M = 8, against 29.5
+    // and 39.3 us on 192 and 256 workgroups).
     auto shape = [&]() {
       cpw = (int)round_up((kcs + want - 1) / want, gc);
       waves = (kcs + cpw - 1) / cpw;
       cps = cpw * waves;
       splits = (p.kc + cps - 1) / cps;
       items = (int64_t)p.tiles * (h16 ? 2 : 1) * splits;
-      grid = (int)std::min<int64_t>(items, force_grid > 0 ? force_grid : grid_cap);
+      if (force_grid > 0) {
+        grid = (int)std::min<int64_t>(items, force_grid);
+      } else {
+        const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
+        grid = (int)((items + rounds - 1) / rounds);
+      }
       per_wg = (items + grid - 1) / grid;
     };
     shape();
-    // One activation row on the MFMA dot (measured on the Qwen3-8B and -32B
-    // projections, medians of repeated graph replays; run-to-run noise is
-    // about 0.3 us):
-    //  * more items than CUs: 192 workgroups, each streaming more items,
-    //    beat 256 (32B QKV 9.5 -> 8.6 us, 8B gate_up 12.7 -> 12.2 us, 32B
-    //    gate_up unchanged); with at most 256 items, one per workgroup;
-    //  * 4 wavefronts instead of 8 when the items split evenly over 256
-    //    workgroups (>= 85% of a whole number of rounds) and each wave would
-    //    cycle through its whole ring of 3 groups: half the data in flight
-    //    per CU, twice the stream per wave (8B down 9.3 -> 8.4 us).
-    // At 8 rows the dot needs the waves and the CUs (every shape slower).
-    // Kept only where the activation still fits the 4-wave quantizing
-    // prologue.
+    // One activation row on the MFMA dot: 4 wavefronts instead of 8 when the
+    // items split evenly over 256 workgroups (>= 85% of a whole number of
+    // rounds) and each wave would cycle through its whole ring of 3 groups:
+    // half the data in flight per CU, twice the stream per wave (8B down
+    // 9.3 -> 8.4 us, medians of repeated graph replays).  At 8 rows the dot
+    // needs the waves and the CUs (every shape slower).  Kept only where the
+    // activation still fits the 4-wave quantizing prologue.
     if (force_waves == 0 && want_mfma && M == 1 && splits == 1 &&
         (int64_t)M * (p.kc * 4) <= nvfp4::qa_max_blocks(4)) {
-      if (force_grid == 0 && items > kStreamGrid) {
-        grid_cap = kStreamGridMany;
-        shape();
-      }
       const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
       const bool even = items * 100 >= rounds * kStreamGrid * 85;
       if (even && per_wg * (cpw / gc) >= 3) {           // 3: the ring depth at M = 1

@@ -52,11 +52,16 @@ constexpr int stream_max_waves(int M) { return M == 1 ? 16 : 8; }
 constexpr int stream_ring_groups(int M) { return M == 3 ? 2 : 3; }
 
 // The MFMA variant keeps 16 result registers per chunk but decodes nothing;
-// its ring has a spare slot (3 groups in flight while it computes, 4 for
-// four or more rows, whose longer epilogue needs the longer lookahead), which
-// needs the 256-register budget of 8 waves.
+// its ring has a spare slot (3 groups in flight while it computes; 2 for four
+// or more rows), which needs the 256-register budget of 8 waves.  The depth is
+// kept low on purpose: the memory system serves the whole grid's requests
+// together, so every request waits behind all the data already in flight
+// (about 6.5 TB/s drains 10 MB per 1.5 us).  At four or more rows the grid
+// runs 8 waves per CU, and 4 groups per wave (38 MB in flight) made every
+// exposed wait, the activation's included, about 6 us long; 2 groups (19 MB)
+// measured faster on every Qwen3 8B / 32B projection at M = 4 and 8.
 constexpr int mfma_max_waves(int) { return 8; }
-constexpr int mfma_ring_groups(int M) { return M >= 4 ? 4 : 3; }
+constexpr int mfma_ring_groups(int M) { return M >= 4 ? 2 : 3; }
 
 // The grid holds at most one workgroup per CU.  The hardware dispatcher
 // packs workgroups onto a CU while its registers and LDS last, so every
@@ -250,11 +255,20 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
   };
 
-  // ---- 2. activation into LDS: the first batch of blocks per thread (loaded
-  // before the weights, see below), any rest (large M * K only) loaded now.
-  // Binary32 product of the two tensor scales (with QA set by the prologue,
-  // which runs before the first item is finished).
-  float g = QA ? 0.0f : __fmul_rn(a.xg[0], a.wg[0]);
+  // ---- 2. activation into LDS.  The memory counter that the waits use
+  // counts loads in issue order, so a wait for an activation load also waits
+  // for every weight load issued before it; all the prologue's loads are
+  // therefore issued before the first weight load, in a fixed number (no
+  // branch between them and the weight loads), and the waits for them leave
+  // the weight loads in flight.  The tensor scales are read at the start,
+  // before the weight loads queue up: a scalar load still outstanding holds
+  // up every later LDS wait, which shares its counter.  An activation too
+  // large for one batch per thread is staged whole before any weight load is
+  // issued.
+  const float wg_v = a.wg[0];
+  const float xg_v = QA ? 0.0f : a.xg[0];
+  const float sgs_v = QA && a.sgs ? a.sgs[0] : 0.0f;
+  float g = 0.0f;                             // the binary32 product of both tensor scales
   uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
   u32x2 xc0[QA ? 1 : kStreamXpt];             // else: its first quantized activation blocks
   uint32_t xs0[QA ? 1 : kStreamXpt];
@@ -355,7 +369,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
     float sg;
     if (a.sgs) {                                      // uniform: a static tensor scale
-      sg = *a.sgs;
+      sg = sgs_v;
     } else {
       amax = wave_max_u32(amax);
       if (lane == 0) wred[wave] = amax;
@@ -364,7 +378,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       for (int w = 0; w < NW; ++w) amax = max(amax, wred[w]);
       sg = tensor_scale(QA == 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
     }
-    g = __fmul_rn(sg, a.wg[0]);
+    g = __fmul_rn(sg, wg_v);
     const bool out = blockIdx.x == 0;
 #pragma unroll
     for (int r = 0; r < kQaBpt; ++r) {
@@ -400,25 +414,12 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
     __syncthreads();
   };
-  auto prologue = [&]() __attribute__((always_inline)) {
-    if constexpr (QA) {
-      quantize_prologue();
-      return;
-    }
-#pragma unroll
-    for (int r = 0; r < kStreamXpt; ++r) {
-      if (r > 0 && nblk <= r * 64 * NW) break;        // rounds that were loaded
-      const int i = threadIdx.x + r * 64 * NW;
-      if (i < nblk) {
-        const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
-        const bool ok = kb < kb_row;
-        put(m, kb, ok ? xc0[r] : u32x2{0u, 0u}, ok ? xs0[r] : 0u);
-      }
-    }
-    // the rest in batches of kStreamXrest blocks per thread, all loads of a
-    // batch in flight together
-    for (int base = threadIdx.x + kStreamXpt * 64 * NW; base < nblk;
-         base += kStreamXrest * 64 * NW) {
+  // QA = 0, an activation of more than one batch: every block staged in
+  // batches of kStreamXrest per thread (all loads of a batch in flight
+  // together), before the weight loads are issued.
+  const bool stage_first = !QA && nblk > kStreamXpt * 64 * NW;
+  auto stage_all = [&]() __attribute__((always_inline)) {
+    for (int base = threadIdx.x; base < nblk; base += kStreamXrest * 64 * NW) {
       u32x2 c[kStreamXrest];
       uint32_t sc[kStreamXrest];
 #pragma unroll
@@ -429,6 +430,9 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         c[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kbc);
         sc[r] = a.xs[(int64_t)m * kb_row + kbc];
       }
+      // keeps the batch's loads above its (conditional) LDS stores: sunk to
+      // their uses they would go out one round trip at a time
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int r = 0; r < kStreamXrest; ++r) {
         const int i = base + r * 64 * NW;
@@ -436,6 +440,24 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
           const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
           const bool ok = kb < kb_row;
           put(m, kb, ok ? c[r] : u32x2{0u, 0u}, ok ? sc[r] : 0u);
+        }
+      }
+    }
+  };
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (QA) {
+      quantize_prologue();
+      return;
+    }
+    g = __fmul_rn(xg_v, wg_v);
+    if (!stage_first) {                               // uniform
+#pragma unroll
+      for (int r = 0; r < kStreamXpt; ++r) {
+        const int i = threadIdx.x + r * 64 * NW;
+        if (i < nblk) {
+          const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
+          const bool ok = kb < kb_row;
+          put(m, kb, ok ? xc0[r] : u32x2{0u, 0u}, ok ? xs0[r] : 0u);
         }
       }
     }
@@ -643,30 +665,31 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   };
 
   static_assert(A >= 2 && A <= 4 && SL <= 5, "ring of 2 to 5 slots");
-  // The activation loads go out before the first weight loads, so waiting
-  // for them does not wait for the weights (addresses clamped into range,
-  // out-of-range blocks zeroed at use: no load is conditional).
+  // The activation loads: a fixed number per thread (addresses clamped into
+  // range, so blocks past the activation reload its last block; such blocks
+  // are skipped or zeroed at use), all before the first weight load.
   if constexpr (QA) {
     const int T = 64 * NW;
     const int nreal = M * kb_row;
-    // only the rounds of T blocks the activation has (a uniform branch: the
-    // weight loads that follow are issued after all of these on every path,
-    // so no wait for an activation block waits for a weight load)
 #pragma unroll
     for (int r = 0; r < kQaBpt; ++r) {
-      if (r > 0 && nreal <= r * T) break;
       const int i = min((int)threadIdx.x + r * T, nreal - 1);
       const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
       load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
     }
+    __asm__ volatile("" ::: "memory");      // issued before the weight loads, not sunk
   } else {
+    if (stage_first) {                                // uniform
+      stage_all();
+    } else {
 #pragma unroll
-    for (int r = 0; r < kStreamXpt; ++r) {
-      if (r > 0 && nblk <= r * 64 * NW) break;        // uniform, as above
-      const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
-      const int m = row_of<M>(i, kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
-      xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
-      xs0[r] = a.xs[(int64_t)m * kb_row + kb];
+      for (int r = 0; r < kStreamXpt; ++r) {
+        const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
+        const int m = row_of<M>(i, kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
+        xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
+        xs0[r] = a.xs[(int64_t)m * kb_row + kb];
+      }
+      __asm__ volatile("" ::: "memory");    // issued before the weight loads, not sunk
     }
   }
   if (ng >= A) {
