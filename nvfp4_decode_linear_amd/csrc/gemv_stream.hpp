@@ -37,8 +37,12 @@ namespace {
 
 using namespace gemv;
 
-constexpr int kStreamXpt = 4;   // activation blocks per thread in the first batch
-constexpr int kStreamXrest = 8; // ... and in each later batch (large M * K)
+// Quantized activation blocks per thread loaded ahead of the weight loads:
+// 4, or 8 at four or more rows (whose shallower ring leaves registers free)
+// when 4 do not cover the activation; larger activations are staged whole
+// before the weight loads.  The count is a kernel variant so that the loads
+// issued are exactly the ones needed.
+constexpr int kXptSmall = 4, kXptLarge = 8;
 constexpr int kQaBpt = 4;       // bf16 blocks per thread when the GEMV quantizes
 
 // Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
@@ -148,7 +152,7 @@ __device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g
 // numbers of outstanding loads merge, it waits for all of them.
 // QA: 0 = the activation arrives quantized; 1 = the prologue quantizes the
 // bf16 activation; 2 = it applies the unweighted per-row RMS norm first.
-template <int M, int RG, int XS, bool MF, bool SPLIT, int QA, bool H16>
+template <int M, int RG, int XS, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   static_assert(!H16 || (MF && !SPLIT), "half tiles: MFMA kernel, one K slice");
   constexpr int GC = H16 ? 8 : 4;             // chunks per ring group
@@ -270,8 +274,8 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const float sgs_v = QA && a.sgs ? a.sgs[0] : 0.0f;
   float g = 0.0f;                             // the binary32 product of both tensor scales
   uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
-  u32x2 xc0[QA ? 1 : kStreamXpt];             // else: its first quantized activation blocks
-  uint32_t xs0[QA ? 1 : kStreamXpt];
+  u32x2 xc0[QA ? 1 : XPT];                    // else: its first quantized activation blocks
+  uint32_t xs0[QA ? 1 : XPT];
   static_assert(QA >= 0 && QA <= 2, "activation prologue mode");
   auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
     if constexpr (MF) {
@@ -414,16 +418,19 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
     __syncthreads();
   };
-  // QA = 0, an activation of more than one batch: every block staged in
-  // batches of kStreamXrest per thread (all loads of a batch in flight
-  // together), before the weight loads are issued.
-  const bool stage_first = !QA && nblk > kStreamXpt * 64 * NW;
-  auto stage_all = [&]() __attribute__((always_inline)) {
-    for (int base = threadIdx.x; base < nblk; base += kStreamXrest * 64 * NW) {
-      u32x2 c[kStreamXrest];
-      uint32_t sc[kStreamXrest];
+  // QA = 0, an activation larger than the first batch: every block staged
+  // before the weight loads are issued (the ring's registers are not live
+  // yet), in batches of B blocks per thread with all of a batch's loads in
+  // flight together: one batch up to 16 blocks per thread (8192 blocks with
+  // 512 threads), else batches of 32.
+  const bool stage_first = !QA && nblk > XPT * 64 * NW;
+  auto stage_batches = [&](auto BB) __attribute__((always_inline)) {
+    constexpr int B = decltype(BB)::value;
+    for (int base = threadIdx.x; base < nblk; base += B * 64 * NW) {
+      u32x2 c[B];
+      uint32_t sc[B];
 #pragma unroll
-      for (int r = 0; r < kStreamXrest; ++r) {
+      for (int r = 0; r < B; ++r) {
         const int i = min(base + r * 64 * NW, nblk - 1);
         const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
         const int kbc = min(kb, kb_row - 1);
@@ -434,7 +441,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       // their uses they would go out one round trip at a time
       __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int r = 0; r < kStreamXrest; ++r) {
+      for (int r = 0; r < B; ++r) {
         const int i = base + r * 64 * NW;
         if (i < nblk) {
           const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
@@ -444,6 +451,10 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       }
     }
   };
+  auto stage_all = [&]() __attribute__((always_inline)) {
+    if (nblk <= 16 * 64 * NW) stage_batches(ic<16>{});
+    else stage_batches(ic<32>{});
+  };
   auto prologue = [&]() __attribute__((always_inline)) {
     if constexpr (QA) {
       quantize_prologue();
@@ -452,7 +463,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     g = __fmul_rn(xg_v, wg_v);
     if (!stage_first) {                               // uniform
 #pragma unroll
-      for (int r = 0; r < kStreamXpt; ++r) {
+      for (int r = 0; r < XPT; ++r) {
         const int i = threadIdx.x + r * 64 * NW;
         if (i < nblk) {
           const int m = row_of<M>(i, kc * 4), kb = i - m * (kc * 4);
@@ -683,7 +694,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       stage_all();
     } else {
 #pragma unroll
-      for (int r = 0; r < kStreamXpt; ++r) {
+      for (int r = 0; r < XPT; ++r) {
         const int i = min((int)threadIdx.x + r * 64 * NW, nblk - 1);
         const int m = row_of<M>(i, kc * 4), kb = min(i - m * (kc * 4), kb_row - 1);
         xc0[r] = *reinterpret_cast<const u32x2*>(a.xc + (int64_t)m * (a.K >> 1) + 8 * kb);
@@ -723,26 +734,26 @@ __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(G
   stream_body<M, stream_ring_groups(M), 0, false, SPLIT, 0, false>(a, lds);
 }
 
-template <int M, bool SPLIT, int QA, bool H16>
+template <int M, bool SPLIT, int QA, bool H16, int XPT>
 __global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA, H16>(a, lds);
+  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA, H16, XPT>(a, lds);
 }
 
-template <int M, bool MF, bool SPLIT, int QA, bool H16>
+template <int M, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall>
 hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch, H16 ? kTileN / 2 : kTileN);
   const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
   const void* fn;
   if constexpr (MF)
-    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA, H16>);
+    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA, H16, XPT>);
   else
     fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M, SPLIT>);
   static hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   if constexpr (MF)
-    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA, H16>), dim3((unsigned)p.grid),
+    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA, H16, XPT>), dim3((unsigned)p.grid),
                        dim3(64 * p.waves), lds, s, a);
   else
     hipLaunchKernelGGL((gemv_stream_kernel<M, SPLIT>), dim3((unsigned)p.grid),
@@ -759,6 +770,11 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
     const int qa = a.xb ? (a.rms ? 2 : 1) : 0;
     if (p.h16) {
       if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
+      if constexpr (M >= 4) {
+        const int nblk = M * p.kc * 4;
+        if (!qa && nblk > kXptSmall * 64 * p.waves && nblk <= kXptLarge * 64 * p.waves)
+          return launch_ms<M, true, false, 0, true, kXptLarge>(p, a, s);
+      }
       return qa == 2   ? launch_ms<M, true, false, 2, true>(p, a, s)
              : qa == 1 ? launch_ms<M, true, false, 1, true>(p, a, s)
                        : launch_ms<M, true, false, 0, true>(p, a, s);
@@ -769,6 +785,12 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
                        : launch_ms<M, true, true, 1, false>(p, a, s);
       return qa == 2 ? launch_ms<M, true, false, 2, false>(p, a, s)
                      : launch_ms<M, true, false, 1, false>(p, a, s);
+    }
+    if constexpr (M >= 4) {
+      const int nblk = M * p.kc * 4;
+      if (nblk > kXptSmall * 64 * p.waves && nblk <= kXptLarge * 64 * p.waves)
+        return p.splits > 1 ? launch_ms<M, true, true, 0, false, kXptLarge>(p, a, s)
+                            : launch_ms<M, true, false, 0, false, kXptLarge>(p, a, s);
     }
   }
   return p.splits > 1 ? launch_ms<M, MF, true, 0, false>(p, a, s)
