@@ -82,7 +82,7 @@ bool split_ok(int M, int cpw, int waves) {
 }
 
 constexpr int64_t kLdsBudget = 160 * 1024;
-constexpr int64_t kFuseMaxBlocks = 2048;
+constexpr int64_t kFuseMaxBlocks = 4096;
 
 void finish_workspace(GemvPlan& p, int M) {
   // The arrival counters live in a fixed region at the start of the
@@ -178,7 +178,7 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     // needs the waves and the CUs (every shape slower).  Kept only where the
     // activation still fits the 4-wave quantizing prologue.
     if (force_waves == 0 && want_mfma && M == 1 && splits == 1 &&
-        (int64_t)M * (p.kc * 4) <= nvfp4::qa_max_blocks(4)) {
+        (int64_t)M * (p.kc * 4) <= nvfp4::qa_max_blocks(M, 4)) {
       const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
       const bool even = items * 100 >= rounds * kStreamGrid * 85;
       if (even && per_wg * (cpw / gc) >= 3) {           // 3: the ring depth at M = 1
@@ -406,12 +406,12 @@ nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, const float*
     return NVFP4_ERR_INVALID_ARG;
   const GemvPlan p = make_plan(M, N, K);
   // Every workgroup quantizes the whole activation in its prologue: worth it
-  // up to 2048 blocks (4 per thread), since the E2M1 encoding runs on the
-  // conversion instruction (with the compare-chain encoder, 2048 blocks ran
-  // slower fused than as two launches).
+  // up to 2048 blocks (4 per thread), and with four or more rows up to 4096
+  // (8 per thread), since the E2M1 encoding runs on the conversion
+  // instruction; the alternative is a second launch (about 5 us at M = 8).
   const int64_t blocks = (int64_t)M * (K >> 4);
   const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
-                     blocks <= nvfp4::qa_max_blocks(p.waves) && blocks <= kFuseMaxBlocks;
+                     blocks <= nvfp4::qa_max_blocks(M, p.waves) && blocks <= kFuseMaxBlocks;
   if (!fused) {
     // two launches: the (RMS norm +) activation quantizer, then the linear
     const nvfp4_status st =

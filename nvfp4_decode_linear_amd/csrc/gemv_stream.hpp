@@ -42,8 +42,9 @@ using namespace gemv;
 // when 4 do not cover the activation; larger activations are staged whole
 // before the weight loads.  The count is a kernel variant so that the loads
 // issued are exactly the ones needed.
+// The same counts give the bf16 blocks per thread of a prologue that
+// quantizes the activation (8 only at four or more rows).
 constexpr int kXptSmall = 4, kXptLarge = 8;
-constexpr int kQaBpt = 4;       // bf16 blocks per thread when the GEMV quantizes
 
 // Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
 // activation row, 8 (<= 256 VGPRs) for two or three rows, whose register
@@ -273,7 +274,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const float xg_v = QA ? 0.0f : a.xg[0];
   const float sgs_v = QA && a.sgs ? a.sgs[0] : 0.0f;
   float g = 0.0f;                             // the binary32 product of both tensor scales
-  uint32_t qv[QA ? kQaBpt : 1][8];            // QA: this thread's bf16 activation blocks
+  uint32_t qv[QA ? XPT : 1][8];            // QA: this thread's bf16 activation blocks
   u32x2 xc0[QA ? 1 : XPT];                    // else: its first quantized activation blocks
   uint32_t xs0[QA ? 1 : XPT];
   static_assert(QA >= 0 && QA <= 2, "activation prologue mode");
@@ -287,7 +288,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
   };
   // QA: the activation quantizer inside the prologue.  Every workgroup reads
-  // the whole bf16 activation (at most kQaBpt blocks per thread, all loads in
+  // the whole bf16 activation (at most XPT blocks per thread, all loads in
   // flight together), takes the exact tensor maximum (bf16 magnitudes as
   // integers: workgroup, then wave, then LDS), and quantizes every block with
   // the quantizer's own arithmetic straight into its LDS staging; workgroup 0
@@ -321,7 +322,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
 #pragma unroll
       for (int m = 0; m < M; ++m) ss[m] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < kQaBpt; ++r) {
+      for (int r = 0; r < XPT; ++r) {
         if (r > 0 && nreal <= r * T) break;           // uniform: no block r here
         const int i = (int)threadIdx.x + r * T;
         const int mr = i < nreal ? row_of<M>(i, kb_row) : M;   // M: no row
@@ -353,9 +354,9 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       __syncthreads();                                  // wss is reused below
     }
     uint32_t amax = 0;
-    uint32_t bmx[kQaBpt];                    // each block's largest magnitude, reused below
+    uint32_t bmx[XPT];                    // each block's largest magnitude, reused below
 #pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {
+    for (int r = 0; r < XPT; ++r) {
       if (r > 0 && nreal <= r * T) break;             // uniform: no block r here
       const int i = (int)threadIdx.x + r * T;
       uint32_t b;
@@ -385,7 +386,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     g = __fmul_rn(sg, wg_v);
     const bool out = blockIdx.x == 0;
 #pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {
+    for (int r = 0; r < XPT; ++r) {
       const int i = (int)threadIdx.x + r * T;
       if (i < nreal) {
         const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
@@ -683,7 +684,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     const int T = 64 * NW;
     const int nreal = M * kb_row;
 #pragma unroll
-    for (int r = 0; r < kQaBpt; ++r) {
+    for (int r = 0; r < XPT; ++r) {
       const int i = min((int)threadIdx.x + r * T, nreal - 1);
       const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
       load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
@@ -766,15 +767,36 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
     return hipErrorInvalidValue;
   if constexpr (MF) {
-    if (a.xb && M * (a.K >> 4) > kQaBpt * 64 * p.waves) return hipErrorInvalidValue;
     const int qa = a.xb ? (a.rms ? 2 : 1) : 0;
+    // blocks the prologue loads per thread: real blocks when it quantizes,
+    // blocks of the padded K when it stages a quantized activation
+    const int nb = qa ? M * (a.K >> 4) : M * p.kc * 4;
+    const bool large = M >= 4 && nb > kXptSmall * 64 * p.waves;
+    if (qa && nb > (M >= 4 ? kXptLarge : kXptSmall) * 64 * p.waves) return hipErrorInvalidValue;
+    if constexpr (M >= 4) {
+      if (large) {
+        if (p.h16) {
+          if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
+          if (!qa && nb > kXptLarge * 64 * p.waves)   // staged whole before the weights
+            return launch_ms<M, true, false, 0, true>(p, a, s);
+          return qa == 2   ? launch_ms<M, true, false, 2, true, kXptLarge>(p, a, s)
+                 : qa == 1 ? launch_ms<M, true, false, 1, true, kXptLarge>(p, a, s)
+                           : launch_ms<M, true, false, 0, true, kXptLarge>(p, a, s);
+        }
+        if (!qa && nb > kXptLarge * 64 * p.waves)
+          return p.splits > 1 ? launch_ms<M, true, true, 0, false>(p, a, s)
+                              : launch_ms<M, true, false, 0, false>(p, a, s);
+        if (p.splits > 1)
+          return qa == 2   ? launch_ms<M, true, true, 2, false, kXptLarge>(p, a, s)
+                 : qa == 1 ? launch_ms<M, true, true, 1, false, kXptLarge>(p, a, s)
+                           : launch_ms<M, true, true, 0, false, kXptLarge>(p, a, s);
+        return qa == 2   ? launch_ms<M, true, false, 2, false, kXptLarge>(p, a, s)
+               : qa == 1 ? launch_ms<M, true, false, 1, false, kXptLarge>(p, a, s)
+                         : launch_ms<M, true, false, 0, false, kXptLarge>(p, a, s);
+      }
+    }
     if (p.h16) {
       if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
-      if constexpr (M >= 4) {
-        const int nblk = M * p.kc * 4;
-        if (!qa && nblk > kXptSmall * 64 * p.waves && nblk <= kXptLarge * 64 * p.waves)
-          return launch_ms<M, true, false, 0, true, kXptLarge>(p, a, s);
-      }
       return qa == 2   ? launch_ms<M, true, false, 2, true>(p, a, s)
              : qa == 1 ? launch_ms<M, true, false, 1, true>(p, a, s)
                        : launch_ms<M, true, false, 0, true>(p, a, s);
@@ -785,12 +807,6 @@ hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
                        : launch_ms<M, true, true, 1, false>(p, a, s);
       return qa == 2 ? launch_ms<M, true, false, 2, false>(p, a, s)
                      : launch_ms<M, true, false, 1, false>(p, a, s);
-    }
-    if constexpr (M >= 4) {
-      const int nblk = M * p.kc * 4;
-      if (nblk > kXptSmall * 64 * p.waves && nblk <= kXptLarge * 64 * p.waves)
-        return p.splits > 1 ? launch_ms<M, true, true, 0, false, kXptLarge>(p, a, s)
-                            : launch_ms<M, true, false, 0, false, kXptLarge>(p, a, s);
     }
   }
   return p.splits > 1 ? launch_ms<M, MF, true, 0, false>(p, a, s)

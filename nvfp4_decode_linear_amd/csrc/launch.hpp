@@ -99,7 +99,7 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               float* ho = nullptr, const float* sgs = nullptr);
 
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
-// (4 bf16 blocks per thread).
-inline int64_t qa_max_blocks(int waves) { return (int64_t)4 * 64 * waves; }
+// (4 bf16 blocks per thread, 8 with four or more rows).
+inline int64_t qa_max_blocks(int M, int waves) { return (int64_t)(M >= 4 ? 8 : 4) * 64 * waves; }
 
 }  // namespace nvfp4

@@ -70,9 +70,11 @@ def _both(nv, x, wq, out_dtype):
     return (y1, q1), (y0, q0)
 
 
+# (the prologue quantizes up to 2048 blocks, 4096 from M = 4: 4096 x 8192 at
+# M = 8 is the largest fused case, 256 x 8704 at M = 8 takes two launches)
 SHAPES = [(256, 512, 1), (6144, 4096, 1), (4096, 4096, 2), (24576, 4096, 4), (4096, 12288, 1),
           (4096, 4096, 8), (100, 1040, 3), (33, 16, 8), (5120, 25600, 1), (10240, 5120, 8),
-          (256, 5632, 8)]
+          (256, 5632, 8), (5120, 8192, 8), (256, 8704, 8), (300, 8192, 5)]
 
 
 @pytest.fixture(params=[0, 1, 2], ids=["tiles_auto", "full_tiles", "half_tiles"])
@@ -140,17 +142,18 @@ def test_fused_strided_input_and_graph_replay(nv):
 
 
 RMS_SHAPES = [(6144, 4096, 1), (24576, 4096, 2), (10240, 5120, 1), (10240, 5120, 3),
-              (51200, 5120, 1), (10240, 5120, 8), (100, 1040, 3), (33, 16, 8), (256, 5632, 8)]
+              (51200, 5120, 1), (10240, 5120, 8), (100, 1040, 3), (33, 16, 8), (256, 5632, 8),
+              (51200, 5120, 8), (256, 8704, 8)]
 U32 = 2.0 ** -24
 
 
 @pytest.mark.parametrize("N,K,M", RMS_SHAPES)
 def test_rmsnorm_quantize_linear(nv, half_tiles, N, K, M):
     """RMS norm, quantization and the linear in one call (one kernel up to
-    2048 activation blocks, else the standalone fused quantizer and the
-    linear): h within the binary32 bound of the oracle, the codes exactly
-    the oracle quantizer of that h, y bit-identical to the linear alone on
-    the written quantized activation."""
+    2048 activation blocks, 4096 from M = 4, else the standalone fused
+    quantizer and the linear): h within the binary32 bound of the oracle, the
+    codes exactly the oracle quantizer of that h, y bit-identical to the
+    linear alone on the written quantized activation."""
     import torch
     note(f"rmsnorm_quantize_linear N={N} K={K} M={M}")
     w16 = weights_bf16(9, N % 7, N, K)
@@ -162,9 +165,11 @@ def test_rmsnorm_quantize_linear(nv, half_tiles, N, K, M):
     _sync()
     hn = h.cpu().numpy()
     ref = oracle.rms_norm_rows(bf16_to_f32(x16).astype(np.float64))
-    # row sums: <= 64 sequential adds per thread (4 blocks), a 6-level wave
-    # tree, <= 7 adds over the waves: 40 u covers the square root and the
-    # five correctly rounded steps, as for the standalone quantizer
+    # row sums: <= 64 sequential adds per thread (a thread holds at most 4
+    # blocks of one row: 2048 blocks per row at most over 512 threads), a
+    # 6-level wave tree, <= 7 adds over the waves: 40 u covers the square
+    # root and the five correctly rounded steps, as for the standalone
+    # quantizer
     assert np.all(np.abs(hn - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
     oq = oracle.quantize(hn)
     assert np.array_equal(q.codes.cpu().numpy(), oq.codes)
