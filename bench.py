@@ -103,6 +103,11 @@ def parse():
     ap.add_argument("--stack-only", action="store_true",
                     help="only the layer stack's decode step (no 8B step, no linear tables); "
                          "prints its own JSON line (for kernel-trace runs of the stack)")
+    ap.add_argument("--kernel-compare", action="store_true",
+                    help="run only the 8B projections' GEMV at M = 1, 2, 3, 8 on the VALU "
+                         "kernels (streaming for M <= 3, split-K for every M) and on the FP4 "
+                         "MFMA kernel, 20 launches each, for rocprofv3 kernel traces; prints "
+                         "the launch order")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only a 256 MiB device copy and a few GEMV launches of the "
                          "timed workload (for rocprofv3 counter runs), print nothing else")
@@ -272,6 +277,10 @@ def main():
             ws = nv.workspace(Mx, L.N, L.K, dev)
     torch.cuda.synchronize()
 
+    if args.kernel_compare:
+        kernel_compare(nv, torch, dev, linears, wsets, xs)
+        return
+
     if args.pmc_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -430,6 +439,29 @@ def main():
     }
     out.update(out_extra)
     print(json.dumps(out), flush=True)
+
+
+def kernel_compare(nv, torch, dev, linears, wsets, xs):
+    """The same GEMVs on each kernel family (NVFP4_OPT_KERNEL: 1 = VALU
+    streaming, M <= 3; 2 = VALU split-K; 3 = FP4 MFMA streaming), 20
+    launches per (M, projection, kernel) over rotated weight copies, so that
+    a rocprofv3 kernel trace gives each kernel's duration per shape."""
+    order = []
+    for M in (1, 2, 3, 8):
+        for li, L in enumerate(linears):
+            xq = nv.quantize_act(xs[li][:M])
+            y = torch.empty((M, L.N), dtype=torch.float32, device=dev)
+            for kern in ((1, 2, 3) if M <= 3 else (2, 3)):
+                nv.set_option("kernel", kern)
+                try:
+                    ws = nv.workspace(M, L.N, L.K, dev)
+                    for c in range(20):
+                        nv.linear(xq, wsets[c % len(wsets)][li], out=y, ws=ws)
+                    torch.cuda.synchronize()
+                finally:
+                    nv.set_option("kernel", 0)
+                order.append(f"M={M} {L.name} kernel={kern}")
+    print("\n".join(order), flush=True)
 
 
 def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
