@@ -25,6 +25,12 @@ Parity status per function (see each docstring for its pins):
       sums, unit-scale integer closed form)
   rms_norm_rows, silu_mul                             pinned (torch CPU library
       routines in float64)
+  reset.token_entropy                                 pinned (closed forms,
+      scipy's entropy of scipy's softmax, invariances)
+  reset.step_update, reset.temperature                parity unpinned (the
+      pages name the step-aware temperature and its hyper-parameters t_low and
+      tau0 but give no formula; the module states the reading used)
+  reset.scale_logits                                  one binary32 division
 """
 
 from .nvfp4 import (  # noqa: F401
@@ -46,4 +52,5 @@ from .nvfp4 import (  # noqa: F401
     tolerance_bound,
     unpack_nibbles,
 )
+from . import reset  # noqa: F401
 from .stack import rms_norm_rows, silu_mul  # noqa: F401
