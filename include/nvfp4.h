@@ -356,6 +356,55 @@ nvfp4_status nvfp4_quantize_linear_noalloc(int M, int64_t N, int64_t K, const ui
                                            uint8_t* x_scales, float* x_gscale, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ReSET's step-aware decoding temperature (the logits processor of the
+ * "ReSET" GitHub README, section "Core components", item 1: the uncertainty
+ * of the current reasoning step is estimated online and the temperature set
+ * from token- and step-level entropy; t_low and tau0 are the per-model
+ * hyper-parameters of the README's "Run benchmarks" command).  The README
+ * gives no formula; this library computes, per logits row m:
+ *   H_m      = entropy in nats of softmax over the row's V logits
+ *              (log sum e^(z - max) - sum e^(z - max) (z - max) / sum e^(z - max),
+ *              binary32, reduced in a fixed order: the same on every run;
+ *              masked logits (-inf) contribute nothing);
+ *   step     = if step_end[m] != 0 (the previous token closed a reasoning
+ *              step) the row's running (sum, count) restarts at (0, 0);
+ *              then sum += H_m, count += 1, H_step = sum / count;
+ *   T_m      = t_low if H_m < tau0, else
+ *              min(t_max, t_base * max(1, H_step / tau0));
+ *   out[m][v] = logits[m][v] / T_m (one correctly rounded division), if
+ *              logits_out is given.
+ * Arguments:
+ *   logits      [M][ldl] binary32, 16-byte aligned, ldl >= V, ldl % 4 == 0;
+ *               every row holds at least one finite logit and no +inf/NaN
+ *   M           1..256 rows;  V >= 1 vocabulary entries per row
+ *   params      host pointer; every field finite and > 0
+ *   step_state  [M][2] device binary32 (running sum, count), zeroed by the
+ *               caller when a sequence starts; updated in place
+ *   step_end    [M] device int32, or NULL (no step ends)
+ *   entropy, temperature  [M] device binary32 outputs
+ *   logits_out  [M][ldo] device binary32, 16-byte aligned, ldo >= V,
+ *               ldo % 4 == 0, or NULL (not written); may be `logits` itself
+ *               (then ldo == ldl), no other overlap
+ *   workspace   nvfp4_reset_workspace_bytes(M, V) bytes, 16-byte aligned,
+ *               zeroed once by nvfp4_workspace_init; every call leaves its
+ *               counters zero again (graph replays need no reset)
+ * Two kernels: the row reductions (the last workgroup of a row to finish
+ * combines the partials and updates the step state) and the division. */
+typedef struct {
+  float t_low;   /* temperature of low-entropy tokens (README example 0.1)  */
+  float tau0;    /* entropy threshold in nats (README example 0.5505)      */
+  float t_base;  /* base temperature of the other tokens                    */
+  float t_max;   /* upper bound of the raised temperature                   */
+} nvfp4_reset_params;
+
+size_t nvfp4_reset_workspace_bytes(int M, int64_t V);
+nvfp4_status nvfp4_reset_temperature(const float* logits, int M, int64_t V, int64_t ldl,
+                                     const nvfp4_reset_params* params, float* step_state,
+                                     const int32_t* step_end, float* entropy, float* temperature,
+                                     float* logits_out, int64_t ldo, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Layer stack: one decode step of an L-layer stack of NVFP4 linears at M
  * rows, captured once into a HIP graph and replayed (the end-to-end figure
  * of the "ReSET" GitHub README, captioned under its introduction, is a

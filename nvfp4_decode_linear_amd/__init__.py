@@ -77,6 +77,18 @@ _rmsnorm_quantize_linear = _sig("nvfp4_rmsnorm_quantize_linear", _c_int, _c_int,
                                 _vp, _vp, _c_size, _vp)
 
 
+class ResetParams(ctypes.Structure):
+    """nvfp4_reset_params: t_low, tau0, t_base, t_max."""
+    _fields_ = [("t_low", ctypes.c_float), ("tau0", ctypes.c_float), ("t_base", ctypes.c_float),
+                ("t_max", ctypes.c_float)]
+
+
+_reset_workspace_bytes = _sig("nvfp4_reset_workspace_bytes", _c_size, _c_int, _c_i64)
+_reset_temperature = _sig("nvfp4_reset_temperature", _c_int, _vp, _c_int, _c_i64, _c_i64,
+                          ctypes.POINTER(ResetParams), _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
+                          _c_size, _vp)
+
+
 class NVFP4Error(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -470,6 +482,44 @@ def rmsnorm_quantize_linear(x, wq: QuantWeight, eps=1e-6, out_dtype=None, out=No
                                     _ptr(q.scales), _ptr(q.gscale), _nullable(h_out), _ptr(ws),
                                     ws.numel(), _stream(y)), "nvfp4_rmsnorm_quantize_linear")
     return y, q
+
+
+def reset_workspace_bytes(M: int, V: int) -> int:
+    return _reset_workspace_bytes(M, V)
+
+
+def reset_temperature(logits, params: ResetParams, state, step_end=None, out=None, ws=None):
+    """ReSET's step-aware temperature for float32 logits [M][V] (row stride
+    a multiple of 4): returns (entropy [M], temperature [M], out) where out
+    is logits / temperature per row (out=None: not computed; out="inplace":
+    written over logits).  state is the float32 [M][2] running (sum, count)
+    of each row's current step, updated in place; step_end an int32 [M]
+    tensor flagging rows whose previous token closed a step."""
+    torch = _torch()
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
+    M, V = logits.shape
+    ent = torch.empty(M, dtype=torch.float32, device=logits.device)
+    tmp = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if isinstance(out, str):
+        if out != "inplace":
+            raise ValueError("out must be None, 'inplace' or a tensor")
+        out = logits
+    ldo = out.stride(0) if out is not None else 0
+    if ws is None:
+        need = reset_workspace_bytes(M, V)
+        dev = logits.device
+        key = ("reset", dev.index if dev.index is not None else torch.cuda.current_device())
+        ws = _WS.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            workspace_init(ws)
+            _WS[key] = ws
+    _check(_reset_temperature(_ptr(logits), M, V, logits.stride(0), ctypes.byref(params),
+                              _ptr(state), _nullable(step_end), _ptr(ent), _ptr(tmp),
+                              _nullable(out), ldo, _ptr(ws), ws.numel(), _stream(logits)),
+           "nvfp4_reset_temperature")
+    return ent, tmp, out
 
 
 def linear(xq: QuantAct, wq: QuantWeight, out_dtype=None, out=None, ws=None):

@@ -545,6 +545,42 @@ size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {
   return make_plan(M, N, K).ws_bytes;
 }
 
+size_t nvfp4_reset_workspace_bytes(int M, int64_t V) {
+  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > (int64_t(1) << 40)) return 0;
+  return nvfp4::kResetCounterBytes +
+         (size_t)round_up((int64_t)M * nvfp4::reset_groups_per_row(V) * 16, 256);
+}
+
+nvfp4_status nvfp4_reset_temperature(const float* logits, int M, int64_t V, int64_t ldl,
+                                     const nvfp4_reset_params* params, float* step_state,
+                                     const int32_t* step_end, float* entropy, float* temperature,
+                                     float* logits_out, int64_t ldo, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!logits || !params || !step_state || !entropy || !temperature)
+    return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > (int64_t(1) << 40) || ldl < V ||
+      ldl % 4 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  const nvfp4_reset_params& q = *params;
+  auto pos = [](float v) { return std::isfinite(v) && v > 0.0f; };
+  if (!pos(q.t_low) || !pos(q.tau0) || !pos(q.t_base) || !pos(q.t_max))
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(logits, 16) || !aligned(step_state, 4) || !aligned(entropy, 4) ||
+      !aligned(temperature, 4) || (step_end && !aligned(step_end, 4)))
+    return NVFP4_ERR_INVALID_ARG;
+  if (logits_out && (ldo < V || ldo % 4 != 0 || !aligned(logits_out, 16) ||
+                     (logits_out == logits && ldo != ldl)))
+    return NVFP4_ERR_INVALID_ARG;
+  const size_t need = nvfp4_reset_workspace_bytes(M, V);
+  if (!workspace || !aligned(workspace, 16)) return NVFP4_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_reset_temperature(
+      logits, M, V, ldl, q.t_low, q.tau0, q.t_base, q.t_max, step_state, step_end, entropy,
+      temperature, logits_out, ldo, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
 nvfp4_status nvfp4_selftest_e2m1(unsigned long long* result, void* stream) {
   if (!result || !aligned(result, 8)) return NVFP4_ERR_INVALID_ARG;
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;

@@ -98,6 +98,17 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               float* og = nullptr, int rms = 0, float eps = 0.0f,
                               float* ho = nullptr, const float* sgs = nullptr);
 
+// ReSET temperature (reset.hip): per-row arrival counters (at most
+// kResetMaxRows rows) at the start of the workspace, then the partial
+// (max, sum, weighted sum) of every workgroup: [rows][groups][4] floats.
+constexpr int kResetMaxRows = 256;
+constexpr size_t kResetCounterBytes = (size_t)kResetMaxRows * 4;
+int reset_groups_per_row(int64_t V);
+hipError_t launch_reset_temperature(const float* z, int M, int64_t V, int64_t ldz, float t_low,
+                                    float tau0, float t_base, float t_max, float* state,
+                                    const int32_t* step_end, float* h_out, float* t_out,
+                                    float* z_out, int64_t ldo, void* workspace, hipStream_t s);
+
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
 // (4 bf16 blocks per thread, 8 with four or more rows).
 inline int64_t qa_max_blocks(int M, int waves) { return (int64_t)(M >= 4 ? 8 : 4) * 64 * waves; }

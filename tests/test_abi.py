@@ -321,3 +321,46 @@ def test_noalloc_argument_errors_and_scratch_size(lib, no_gpu):
         assert f(8, 65536, 32768, FAKE, 32768, *ok) == 4
     finally:
         assert lib.nvfp4_set_option(1, 0) == 0
+
+
+def test_reset_temperature_argument_errors(lib, no_gpu):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+
+    class P(ctypes.Structure):
+        _fields_ = [("t_low", ctypes.c_float), ("tau0", ctypes.c_float),
+                    ("t_base", ctypes.c_float), ("t_max", ctypes.c_float)]
+
+    w = lib.nvfp4_reset_workspace_bytes
+    w.argtypes = [ctypes.c_int, i64]
+    w.restype = ctypes.c_size_t
+    # 1 KiB of row counters, then 16 B per (row, group of 4096 logits),
+    # rounded up to 256 B: the Qwen3 vocabulary (151936) has 38 groups
+    assert w(1, 151936) == 1024 + 768
+    assert w(8, 151936) == 1024 + 4864
+    assert w(0, 10) == 0 and w(257, 10) == 0 and w(1, 0) == 0
+    f = lib.nvfp4_reset_temperature
+    f.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.POINTER(P), vp, vp, vp, vp, vp, i64, vp,
+                  ctypes.c_size_t, vp]
+    good = P(0.1, 0.5505, 0.6, 1.5)
+    ok_tail = (FAKE, None, FAKE, FAKE, None, 0, FAKE, 1 << 20, None)
+    assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *ok_tail) == 3          # no device
+    assert f(FAKE, 0, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
+    assert f(FAKE, 257, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
+    assert f(FAKE, 1, 1000, 999, ctypes.byref(good), *ok_tail) == 1           # ldl < V
+    assert f(FAKE, 1, 1000, 1002, ctypes.byref(good), *ok_tail) == 1          # ldl % 4
+    assert f(ctypes.c_void_p(0x1008), 1, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
+    assert f(FAKE, 1, 1000, 1000, None, *ok_tail) == 1                        # no params
+    for bad in (P(0.0, 0.5, 0.6, 1.5), P(0.1, -1.0, 0.6, 1.5), P(0.1, 0.5, float("nan"), 1.5),
+                P(0.1, 0.5, 0.6, float("inf"))):
+        assert f(FAKE, 1, 1000, 1000, ctypes.byref(bad), *ok_tail) == 1
+    tail = list(ok_tail)
+    tail[6] = None                                                            # no workspace
+    assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 1
+    tail = list(ok_tail)
+    tail[7] = 16                                                              # too small
+    assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 4
+    tail = list(ok_tail)
+    tail[4], tail[5] = FAKE, 1000                                             # in place, ldo == ldl
+    assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 3
+    tail[5] = 1004                                                            # in place, ldo != ldl
+    assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 1
