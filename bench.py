@@ -480,12 +480,15 @@ def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
         for L in lins:
             w = (torch.randn((L.N, L.K), generator=gen, device=dev, dtype=torch.float32)
                  * 0.02).to(torch.bfloat16)
-            layer.append(nv.quantize_weight(w))
+            # gate_up in the interleaved row order of the SiLU * mul epilogue
+            layer.append(nv.quantize_weight_gate_up(w) if L.name == "gate_up"
+                         else nv.quantize_weight(w))
             del w
         seeds.append(layer)
     nl = args.stack_layers
     layers = [seeds[l] if l < 2 else
-              [nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N, w.K)
+              [nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N, w.K,
+                              w.gate_up)
                for w in seeds[l % 2]] for l in range(nl)]
     torch.cuda.synchronize()
     wbytes = sum(w.codes.numel() + w.scales.numel() for w in layers[0])

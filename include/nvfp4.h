@@ -122,7 +122,12 @@ typedef enum {
                                  (default) = when 32-row tiles fill at most
                                  half the 256 workgroups, 1 = never, 2 =
                                  always (one K slice only).                */
-  NVFP4_OPT_COUNT = 10
+  NVFP4_OPT_F32_SLICES = 10,  /* nvfp4_quantize_linear_f32 given a maxima
+                                 record: 0 (default) = never use the K-slice
+                                 plan (two launches when the activation does
+                                 not fit one prologue), 1 = only then, 2 =
+                                 always (where a slice plan exists).       */
+  NVFP4_OPT_COUNT = 11
 } nvfp4_option;
 
 /* ABI version of this header (incremented on any signature change). */
@@ -156,6 +161,18 @@ nvfp4_status nvfp4_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_
 nvfp4_status nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t N, int64_t K, int64_t ldw,
                                    uint8_t* w_codes, uint8_t* w_scales, float* w_gscale,
                                    void* stream);
+
+/* The gate_up weight [2F][K] (rows [0, F) gate, [F, 2F) up) quantized as
+ * nvfp4_quantize_weight would, into the interleaved row order the SiLU * mul
+ * epilogue reads (nvfp4_quantize_linear_silu_mul): tiled row 32t + r holds
+ * source row 16t + r for r < 16 and F + 16t + r - 16 for r >= 16, so each
+ * 32-row tile carries the gate and up rows of the same 16 output columns.
+ * The result is exactly nvfp4_quantize_weight of the rows in that order
+ * (the tensor scale does not depend on row order).  F % 16 == 0; the rest
+ * as for nvfp4_quantize_weight with N = 2F. */
+nvfp4_status nvfp4_quantize_weight_gate_up(const uint16_t* w_bf16, int64_t F, int64_t K,
+                                           int64_t ldw, uint8_t* w_codes, uint8_t* w_scales,
+                                           float* w_gscale, void* stream);
 
 /* Inverse of the tiling: device-tiled weight -> canonical row-major codes
  * [N][K/2] and scales [N][K/16] (for export and bit-exact checks). */
@@ -219,7 +236,8 @@ nvfp4_status nvfp4_quantize_linear_static(int M, int64_t N, int64_t K, const uin
  * bit-identical to nvfp4_quantize_act(x_bf16 -> x_codes, x_scales,
  * x_gscale) followed by nvfp4_linear on those outputs, which this call also
  * writes.  When the plan streams the weights on the MFMA kernel and M * K /
- * 16 <= 2048, a single kernel does both: every workgroup quantizes the
+ * 16 <= 2048 (4096 with M >= 4, at most 4 (8) blocks per thread of the
+ * plan's workgroup), a single kernel does both: every workgroup quantizes the
  * activation in its prologue (reading the bf16 input from L2) and workgroup
  * 0 writes the quantized copy, so the separate quantizer launch disappears;
  * otherwise (or with NVFP4_OPT_FUSE_QUANT = 0) the two launches run in
@@ -289,6 +307,79 @@ nvfp4_status nvfp4_silu_mul_quantize_act(const uint16_t* gu_bf16, int M, int64_t
                                          uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
                                          float* h_out, void* workspace, size_t workspace_bytes,
                                          void* stream);
+
+/* SiLU * mul fused into the gate_up projection, and the down projection fed
+ * from its binary32 output (the layer step between the two linears, with no
+ * separate quantizer launch: "ReSET" GitHub README, "Core components" item
+ * 2, the W4A4 decode linear; the SiLU * mul step as in the stack above).
+ *
+ * A maxima record is NVFP4_AMAX_RECORD_WORDS uint32 words, 16-byte aligned:
+ * word i holds the largest |h| (binary32 bit pattern, sign cleared) of the
+ * h values one workgroup wrote, zero for unused words, so the tensor maximum
+ * of h is the record's largest word.  It lets the consumer take the tensor
+ * scale without a pass over h. */
+#define NVFP4_AMAX_RECORD_WORDS 256
+
+/* gate_up linear + SiLU * mul:
+ *   g = bf16(y[m][j]), u = bf16(y[m][F + j]),  h[m][j] = silu(g) * u  (j < F)
+ * with y the linear of Q(x) (rmsnorm = 0) or of Q(rmsnorm(x)) (rmsnorm = 1,
+ * h of the norm as in nvfp4_rmsnorm_quantize_linear) with the gate_up weight
+ * [2F][K] (rows [0, F) gate, [F, 2F) up), the bf16 rounding the one the
+ * linear's bf16 output applies, and silu(g) * u the element operation of
+ * nvfp4_silu_mul_quantize_act.  So h is bit-identical to the h_out of
+ * nvfp4_silu_mul_quantize_act on g and u (gu_out).
+ *   x_bf16   [M][ldx] bf16 as for nvfp4_quantize_linear; eps as for the RMS norm
+ *   w_*      the gate_up weight from nvfp4_quantize_weight_gate_up (the
+ *            interleaved row order); F % 16 == 0
+ *   h        binary32 [M][ldh], ldh >= F, ldh % 4 == 0, 16-byte aligned
+ *   h_amax   the maxima record of h (written whole)
+ *   gu_out   optional (NULL: not written) bf16 [M][2F]: g and u as above
+ *   x_codes, x_scales, x_gscale  the quantized activation (written)
+ *   xh_out   optional binary32 [M][K]: the normalised input (rmsnorm = 1 only)
+ *   workspace  at least 16 bytes when M > 1 (used only when the activation
+ *            is quantized by its own launch first; left zero)
+ * One kernel when the activation fits the GEMV's quantizing prologue (as for
+ * nvfp4_quantize_linear), else the quantizer then the GEMV.  The GEMV runs
+ * on whole 32-row tiles with one K slice (each tile holds both factors of
+ * its 16 columns); NVFP4_ERR_UNSUPPORTED if no such plan fits. */
+nvfp4_status nvfp4_quantize_linear_silu_mul(int M, int64_t F, int64_t K, const uint16_t* x_bf16,
+                                            int64_t ldx, int rmsnorm, float eps,
+                                            const uint8_t* w_codes, const uint8_t* w_scales,
+                                            const float* w_gscale, float* h, int64_t ldh,
+                                            uint32_t* h_amax, uint16_t* gu_out, uint8_t* x_codes,
+                                            uint8_t* x_scales, float* x_gscale, float* xh_out,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/* The activation quantizer Q on a binary32 activation x_f32 [M][ldx] (ldx >=
+ * K, ldx % 4 == 0, 16-byte aligned): the quantizer steps of
+ * nvfp4_quantize_act starting from binary32 values.  x_amax: NULL, or the
+ * maxima record of x_f32 written by its producer (then the tensor maximum is
+ * read from it and no workspace is needed); without it the workspace holds
+ * the 16-byte sync record of nvfp4_quantize_act. */
+nvfp4_status nvfp4_quantize_act_f32(const float* x_f32, int M, int64_t K, int64_t ldx,
+                                    const uint32_t* x_amax, uint8_t* x_codes, uint8_t* x_scales,
+                                    float* x_gscale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* nvfp4_quantize_act_f32 and nvfp4_linear in one call (x_codes, x_scales,
+ * x_gscale written).  One kernel when the activation fits the quantizing
+ * prologue (M * K / 16 <= 4 blocks per thread of the plan's workgroup, and
+ * <= 4096), on nvfp4_linear's own plan: y is then bit-identical to
+ * nvfp4_linear on the written codes.  Otherwise the two launches (the
+ * quantizer then nvfp4_linear), unless NVFP4_OPT_F32_SLICES selects the
+ * K-slice plan (x_amax required): a split-K plan whose workgroups each stay
+ * in one K slice and quantize only that slice, the tensor scale taken from
+ * the record, workgroup s < splits writing slice s's codes.  The workspace
+ * must hold nvfp4_quantize_linear_f32_workspace_bytes(M, N, K) (the largest
+ * need of the paths the current options allow), zero-initialised. */
+size_t nvfp4_quantize_linear_f32_workspace_bytes(int M, int64_t N, int64_t K);
+nvfp4_status nvfp4_quantize_linear_f32(int M, int64_t N, int64_t K, const float* x_f32,
+                                       int64_t ldx, const uint32_t* x_amax,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const float* w_gscale, void* y, int out_dtype,
+                                       uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes nvfp4_linear needs for this shape under the current
  * options: 0 when K is not split, else a fixed 64 KiB region of split-K
@@ -414,7 +505,11 @@ nvfp4_status nvfp4_reset_temperature(const float* logits, int M, int64_t V, int6
  *   -> quantize the first q_cols columns of its output -> O linear
  *   -> RMS norm + quantize -> gate_up linear (2 * ffn outputs)
  *   -> SiLU * mul + quantize (nvfp4_silu_mul_quantize_act) -> down linear,
- * whose output is the next layer's input.  Every linear writes bf16.  The
+ * whose output is the next layer's input.  With gate_up_interleaved set the
+ * gate_up linear and SiLU * mul are one call (nvfp4_quantize_linear_silu_mul)
+ * and the quantizer of h runs in the down GEMV (nvfp4_quantize_linear_f32
+ * with the maxima record), four kernels per layer when every quantizer fits
+ * its GEMV's prologue.  Every linear writes bf16.  The
  * stack has no attention, residual or norm weights (out of scope: only the
  * linears and the quantizers between them are modelled).
  */
@@ -435,6 +530,9 @@ typedef struct {
   int64_t q_cols;   /* leading QKV output columns that feed O (K of O)         */
   int64_t ffn;      /* gate_up has 2 * ffn outputs (gate first); K of down     */
   float eps;        /* RMS norm epsilon, 0 <= eps < 1                          */
+  int gate_up_interleaved; /* 1: the gate_up weights come from
+                      nvfp4_quantize_weight_gate_up (SiLU * mul fused);
+                      0: from nvfp4_quantize_weight (SiLU * mul on its own) */
 } nvfp4_stack_config;
 
 /* Create a stack: weights[4 * l + j] is layer l's QKV (j = 0, qkv_n x hidden),

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_WORKSPACE, ERR_HIP = range(6)
 OUT_F32, OUT_BF16 = 0, 1
 OPTIONS = {"gemv_max_m": 0, "split_k": 1, "chunks_per_wave": 2, "nontemporal": 3, "waves": 4,
-           "kernel": 5, "spin_limit": 6, "grid": 7, "fuse_quant": 8, "half_tiles": 9}
+           "kernel": 5, "spin_limit": 6, "grid": 7, "fuse_quant": 8, "half_tiles": 9,
+           "f32_slices": 10}
 TILE_N, CHUNK_K, GROUP_K = 32, 64, 256
 
 if not os.path.exists(LIB_PATH):
@@ -75,6 +76,21 @@ _quantize_linear_noalloc = _sig("nvfp4_quantize_linear_noalloc", _c_int, _c_int,
 _rmsnorm_quantize_linear = _sig("nvfp4_rmsnorm_quantize_linear", _c_int, _c_int, _c_i64, _c_i64, _vp,
                                 _c_i64, ctypes.c_float, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
                                 _vp, _vp, _c_size, _vp)
+
+
+_quantize_weight_gate_up = _sig("nvfp4_quantize_weight_gate_up", _c_int, _vp, _c_i64, _c_i64,
+                                _c_i64, _vp, _vp, _vp, _vp)
+_quantize_act_f32 = _sig("nvfp4_quantize_act_f32", _c_int, _vp, _c_int, _c_i64, _c_i64, _vp, _vp,
+                         _vp, _vp, _vp, _c_size, _vp)
+_quantize_linear_f32 = _sig("nvfp4_quantize_linear_f32", _c_int, _c_int, _c_i64, _c_i64, _vp,
+                            _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_size,
+                            _vp)
+_quantize_linear_f32_workspace_bytes = _sig("nvfp4_quantize_linear_f32_workspace_bytes", _c_size,
+                                            _c_int, _c_i64, _c_i64)
+_quantize_linear_silu_mul = _sig("nvfp4_quantize_linear_silu_mul", _c_int, _c_int, _c_i64, _c_i64,
+                                 _vp, _c_i64, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _c_i64,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp)
+AMAX_RECORD_WORDS = 256
 
 
 class ResetParams(ctypes.Structure):
@@ -159,6 +175,7 @@ class QuantWeight:
     gscale: object     # float32 tensor [1]
     N: int
     K: int
+    gate_up: bool = False   # rows interleaved for the SiLU * mul epilogue
 
 
 @dataclass
@@ -189,6 +206,20 @@ def quantize_weight(w, out: QuantWeight | None = None) -> QuantWeight:
     _check(_quantize_weight(_ptr(w), N, K, w.stride(0), _ptr(q.codes), _ptr(q.scales),
                             _ptr(q.gscale), _stream(w)), "nvfp4_quantize_weight")
     return q
+
+
+def quantize_weight_gate_up(w, out: QuantWeight | None = None) -> QuantWeight:
+    """bf16 gate_up weight [2F][K] (gate rows first) -> device-tiled NVFP4
+    weight in the interleaved row order of the SiLU * mul epilogue."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1 or w.shape[0] % 2:
+        raise ValueError("w must be a 2-D bf16 tensor [2F][K] with unit column stride")
+    N, K = w.shape
+    q = out if out is not None else empty_weight(N, K, w.device)
+    _check(_quantize_weight_gate_up(_ptr(w), N // 2, K, w.stride(0), _ptr(q.codes),
+                                    _ptr(q.scales), _ptr(q.gscale), _stream(w)),
+           "nvfp4_quantize_weight_gate_up")
+    return QuantWeight(q.codes, q.scales, q.gscale, N, K, True)
 
 
 def selftest_e2m1(device="cuda"):
@@ -289,7 +320,7 @@ def silu_mul_quantize_act(gu, out: QuantAct | None = None, h_out=None, ws=None):
 class _StackConfig(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int), ("layers", ctypes.c_int), ("hidden", ctypes.c_int64),
                 ("qkv_n", ctypes.c_int64), ("q_cols", ctypes.c_int64), ("ffn", ctypes.c_int64),
-                ("eps", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("gate_up_interleaved", ctypes.c_int)]
 
 
 class _Weight(ctypes.Structure):
@@ -316,7 +347,11 @@ class Stack:
         torch = _torch()
         self._torch = torch
         self._h = None
-        self.cfg = _StackConfig(M, len(layers), hidden, qkv_n, q_cols, ffn, eps)
+        inter = [bool(ws4[2].gate_up) for ws4 in layers]
+        if any(inter) != all(inter):
+            raise ValueError("gate_up weights: all interleaved or none")
+        self.cfg = _StackConfig(M, len(layers), hidden, qkv_n, q_cols, ffn, eps,
+                                1 if all(inter) else 0)
         arr = (_Weight * (4 * len(layers)))()
         for l, ws4 in enumerate(layers):
             for j, w in enumerate(ws4):
@@ -363,10 +398,12 @@ class Stack:
 _WS = {}
 
 
-def workspace(M: int, N: int, K: int, device="cuda"):
-    """A per-device workspace, grown and zero-initialised on demand."""
+def workspace(M: int, N: int, K: int, device="cuda", need: int | None = None):
+    """A per-device workspace, grown and zero-initialised on demand (need:
+    bytes, default the linear's)."""
     torch = _torch()
-    need = linear_workspace_bytes(M, N, K)
+    if need is None:
+        need = linear_workspace_bytes(M, N, K)
     dev = torch.device(device)
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
     ws = _WS.get(key)
@@ -482,6 +519,80 @@ def rmsnorm_quantize_linear(x, wq: QuantWeight, eps=1e-6, out_dtype=None, out=No
                                     _ptr(q.scales), _ptr(q.gscale), _nullable(h_out), _ptr(ws),
                                     ws.numel(), _stream(y)), "nvfp4_rmsnorm_quantize_linear")
     return y, q
+
+
+def quantize_act_f32(x, amax=None, out: QuantAct | None = None, ws=None) -> QuantAct:
+    """Quantize a float32 activation [M][K] (row stride a multiple of 4);
+    amax: the producer's uint32 maxima record, or None."""
+    torch = _torch()
+    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 tensor with unit column stride")
+    M, K = x.shape
+    q = out if out is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(M, 1, K, x.device, need=256)
+    _check(_quantize_act_f32(_ptr(x), M, K, x.stride(0), _nullable(amax), _ptr(q.codes),
+                             _ptr(q.scales), _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(x)),
+           "nvfp4_quantize_act_f32")
+    return q
+
+
+def quantize_linear_f32(x, wq: QuantWeight, amax=None, out_dtype=None, out=None,
+                        xq: QuantAct | None = None, ws=None):
+    """Quantize float32 x [M][K] and apply the NVFP4 linear (one kernel when
+    possible; with the producer's maxima record `amax` also for activations
+    too large for one workgroup's prologue); returns (y, xq)."""
+    torch = _torch()
+    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 tensor with unit column stride")
+    M, K = x.shape
+    if K != wq.K:
+        raise ValueError("K mismatch")
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    y = out if out is not None else torch.empty((M, wq.N), dtype=out_dtype, device=x.device)
+    q = xq if xq is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(M, wq.N, K, x.device,
+                       need=_quantize_linear_f32_workspace_bytes(M, wq.N, K))
+    _check(_quantize_linear_f32(M, wq.N, K, _ptr(x), x.stride(0), _nullable(amax), _ptr(wq.codes),
+                                _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), od, _ptr(q.codes),
+                                _ptr(q.scales), _ptr(q.gscale), _ptr(ws), ws.numel(), _stream(y)),
+           "nvfp4_quantize_linear_f32")
+    return y, q
+
+
+def quantize_linear_silu_mul(x, wq: QuantWeight, rmsnorm=False, eps=1e-6, h=None, amax=None,
+                             gu_out=None, xq: QuantAct | None = None, xh_out=None, ws=None):
+    """gate_up linear of bf16 x [M][K] (RMS-normalised first with rmsnorm)
+    with SiLU * mul applied in its epilogue: wq is the gate_up weight [2F][K];
+    returns (h [M][F] float32, amax record [256] int32 holding uint32 words,
+    xq)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    M, K = x.shape
+    if K != wq.K or wq.N % 2 or not wq.gate_up:
+        raise ValueError("wq must be a gate_up weight from quantize_weight_gate_up with K = x's")
+    F = wq.N // 2
+    h = h if h is not None else torch.empty((M, F), dtype=torch.float32, device=x.device)
+    if h.dtype != torch.float32 or h.dim() != 2 or h.stride(1) != 1 or h.shape != (M, F):
+        raise ValueError("h must be a float32 [M][F] tensor with unit column stride")
+    amax = amax if amax is not None else torch.empty(AMAX_RECORD_WORDS, dtype=torch.int32,
+                                                     device=x.device)
+    q = xq if xq is not None else empty_act(M, K, x.device)
+    if ws is None:
+        ws = workspace(M, 1, K, x.device, need=256)
+    _check(_quantize_linear_silu_mul(M, F, K, _ptr(x), x.stride(0), 1 if rmsnorm else 0,
+                                     float(eps), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale),
+                                     _ptr(h), h.stride(0), _ptr(amax), _nullable(gu_out),
+                                     _ptr(q.codes), _ptr(q.scales), _ptr(q.gscale),
+                                     _nullable(xh_out), _ptr(ws), ws.numel(), _stream(h)),
+           "nvfp4_quantize_linear_silu_mul")
+    return h, amax, q
 
 
 def reset_workspace_bytes(M: int, V: int) -> int:

@@ -24,7 +24,8 @@ constexpr int kLayoutVersion = 1;
 constexpr int kMaxM = 8;
 constexpr int kMaxDevices = 64;
 
-std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0}, {0}, {0}, {0}, {1}, {0}};
+std::atomic<int64_t> g_opts[NVFP4_OPT_COUNT] = {{0}, {0}, {0}, {1}, {0},
+                                                {0}, {0}, {0}, {1}, {0}, {0}};
 thread_local int t_last_hip = 0;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -39,6 +40,7 @@ namespace nvfp4 {
 // for the other host translation units of the library (stack.cpp)
 nvfp4_status record_hip_error(hipError_t e) { return hip_fail(e); }
 }  // namespace nvfp4
+static_assert(NVFP4_AMAX_RECORD_WORDS == nvfp4::kAmaxSlots, "maxima record size");
 
 namespace {
 
@@ -116,7 +118,13 @@ int stream_splits(int tiles, int kc) {
 }
 
 // Launch plan of the GEMV for (M, N, K) under the current knobs.
-GemvPlan make_plan(int M, int64_t N, int64_t K) {
+//   silu: the gate_up projection with the SiLU * mul epilogue (MFMA, whole
+//         row tiles, one K slice)
+//   slices: that many K slices (MFMA, whole tiles) on a grid that is a
+//         multiple of them, so that every workgroup stays in one slice
+// Either returns a plan of kind kGemvSplit when the streaming kernel cannot
+// take the shape.
+GemvPlan make_plan(int M, int64_t N, int64_t K, bool silu = false, int slices = 0) {
   GemvPlan p = {};
   p.kc = (int)(round_up(K, nvfp4::kGroupK) / nvfp4::kChunkK);
   p.tiles = (int)(round_up(N, nvfp4::kTileN) / nvfp4::kTileN);
@@ -131,7 +139,9 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
   // dot (M <= 3 only), larger M the MFMA dot.
   const int64_t gemv_max_m = g_opts[NVFP4_OPT_GEMV_MAX_M].load();
   const bool auto_kind = force_kernel == 0 && force_cpw == 0;
-  const bool want_mfma = force_kernel == 3 || (auto_kind && (M > gemv_max_m || M > 3));
+  const bool special = silu || slices > 0;
+  const bool want_mfma =
+      special || force_kernel == 3 || (auto_kind && (M > gemv_max_m || M > 3));
   const bool want_valu = !want_mfma && (force_kernel == 1 || auto_kind) && M <= 3;
   if (want_mfma || want_valu) {
     const int max_waves = want_mfma ? 8 : (M == 1 ? 16 : 8);  // as compiled
@@ -140,10 +150,13 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     // 16-row half tiles (MFMA only, one K slice): twice the work items, for
     // shapes whose 32-row tiles leave CUs idle.
     const int64_t force_half = g_opts[NVFP4_OPT_HALF_TILES].load();
-    const bool h16 = want_mfma && force_split <= 1 &&
+    const bool h16 = !special && want_mfma && force_split <= 1 &&
                      (force_half == 2 || (force_half == 0 && 2 * p.tiles <= kStreamGrid));
     const int gc = h16 ? 8 : 4;                              // chunks per ring group
-    const int s0 = h16 ? 1 : force_split > 0 ? (int)force_split : stream_splits(p.tiles, p.kc);
+    const int s0 = h16 || silu      ? 1
+                   : slices > 0     ? slices
+                   : force_split > 0 ? (int)force_split
+                                     : stream_splits(p.tiles, p.kc);
     const int kcs = (p.kc + s0 - 1) / s0;                 // chunks per slice
     const int64_t force_grid = g_opts[NVFP4_OPT_GRID].load();
     int cpw, waves, cps, splits, grid;
@@ -161,13 +174,23 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
       cps = cpw * waves;
       splits = (p.kc + cps - 1) / cps;
       items = (int64_t)p.tiles * (h16 ? 2 : 1) * splits;
-      if (force_grid > 0) {
+      if (slices > 0) {
+        // gt workgroups per slice, each over tiles b, b + gt, ...
+        int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid, gt;
+        for (;; ++rounds) {
+          gt = ((int64_t)p.tiles + rounds - 1) / rounds;
+          if (gt * splits <= kStreamGrid) break;
+        }
+        grid = (int)(gt * splits);
+        per_wg = ((int64_t)p.tiles + gt - 1) / gt;
+      } else if (force_grid > 0) {
         grid = (int)std::min<int64_t>(items, force_grid);
+        per_wg = (items + grid - 1) / grid;
       } else {
         const int64_t rounds = (items + kStreamGrid - 1) / kStreamGrid;
         grid = (int)((items + rounds - 1) / rounds);
+        per_wg = (items + grid - 1) / grid;
       }
-      per_wg = (items + grid - 1) / grid;
     };
     shape();
     // One activation row on the MFMA dot: 4 wavefronts instead of 8 when the
@@ -189,7 +212,9 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
     const int64_t act = (int64_t)nvfp4::stream_act_lds(M, p.kc, want_mfma);
     const int64_t slot = (int64_t)waves * M * (h16 ? 16 : 32) * 4;
     const int64_t batch = std::min<int64_t>(per_wg, (kLdsBudget - act) / slot);
-    if (waves <= max_waves && batch >= 1 &&
+    const bool shape_ok = !silu || N % nvfp4::kTileN == 0;
+    const bool slices_ok = slices == 0 || (splits > 1 && grid % splits == 0);
+    if (waves <= max_waves && batch >= 1 && shape_ok && slices_ok &&
         (splits == 1 || per_wg <= batch * waves * M * 32)) {
       p.kind = want_mfma ? nvfp4::kGemvMfma : nvfp4::kGemvStream;
       p.waves = waves;
@@ -207,6 +232,7 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
 
   // Split kernel: one workgroup per (row tile, K slice).
   p.kind = nvfp4::kGemvSplit;
+  if (special) return p;                  // no streaming plan for the fused epilogue / slices
   p.depth = 0;
   int waves = force_waves > 0 ? (int)force_waves : 4;
   int cpw = 4;
@@ -237,6 +263,13 @@ GemvPlan make_plan(int M, int64_t N, int64_t K) {
 }
 
 }  // namespace
+
+namespace nvfp4 {
+// for stack.cpp: whether the gate_up GEMV with the SiLU * mul epilogue has a plan
+bool silu_plan_ok(int M, int64_t F, int64_t K) {
+  return F >= 16 && F % 16 == 0 && make_plan(M, 2 * F, K, true).kind == kGemvMfma;
+}
+}  // namespace nvfp4
 
 extern "C" {
 
@@ -286,6 +319,7 @@ nvfp4_status nvfp4_set_option(int opt, int64_t value) {
       if (value != 0 && value != 1) return NVFP4_ERR_INVALID_ARG;
       break;
     case NVFP4_OPT_HALF_TILES:
+    case NVFP4_OPT_F32_SLICES:
       if (value < 0 || value > 2) return NVFP4_ERR_INVALID_ARG;
       break;
     default: return NVFP4_ERR_UNSUPPORTED;
@@ -320,6 +354,21 @@ nvfp4_status nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t N, int64_t K,
   if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
   const hipError_t e = nvfp4::launch_quantize_weight(w_bf16, N, K, ldw, w_codes, w_scales,
                                                      w_gscale, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_quantize_weight_gate_up(const uint16_t* w_bf16, int64_t F, int64_t K,
+                                           int64_t ldw, uint8_t* w_codes, uint8_t* w_scales,
+                                           float* w_gscale, void* stream) {
+  if (!w_bf16 || !w_codes || !w_scales || !w_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (F < 16 || F % 16 != 0 || !valid_nk(2 * F, K) || ldw < K || ldw % 8 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(w_bf16, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
+      !aligned(w_gscale, 4))
+    return NVFP4_ERR_INVALID_ARG;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_quantize_weight(w_bf16, 2 * F, K, ldw, w_codes, w_scales,
+                                                     w_gscale, (hipStream_t)stream, F);
   return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
@@ -488,6 +537,192 @@ nvfp4_status nvfp4_rmsnorm_quantize_linear(int M, int64_t N, int64_t K, const ui
   return quantize_linear_impl(1, eps, h_out, nullptr, M, N, K, x_bf16, ldx, w_codes, w_scales,
                               w_gscale, y, out_dtype, x_codes, x_scales, x_gscale, workspace,
                               workspace_bytes, stream);
+}
+
+namespace {
+
+// Fraction of the 256 CUs' item slots a streaming plan fills.
+double plan_eff(const GemvPlan& p) {
+  const int64_t items = (int64_t)p.tiles * (p.h16 ? 2 : 1) * p.splits;
+  const int64_t per_wg = (items + p.grid - 1) / p.grid;
+  return (double)items / (double)(kStreamGrid * per_wg);
+}
+
+// The K-slice plan of the binary32 quantize + linear: among 2..16 slices
+// whose per-slice blocks fit the prologue, the one that keeps the most CUs
+// busy (items / (256 x items per workgroup)), the fewest slices on a tie;
+// kind kGemvSplit if none fits.  (Qwen3-32B down at M = 8: 8 slices of 56
+// chunks on 256 workgroups; 7 slices would leave 32 CUs idle.)
+GemvPlan f32_slice_plan(int M, int64_t N, int64_t K) {
+  GemvPlan best = {};
+  best.kind = nvfp4::kGemvSplit;
+  double best_eff = 0.0;
+  for (int sl = 2; sl <= 16; ++sl) {
+    const GemvPlan p = make_plan(M, N, K, false, sl);
+    if (p.kind != nvfp4::kGemvMfma) continue;
+    const int64_t blocks = (int64_t)M * std::min<int64_t>(4 * (int64_t)p.cps, K >> 4);
+    if (blocks > nvfp4::qa_max_blocks(M, p.waves, true)) continue;
+    const double eff = plan_eff(p);
+    if (eff > best_eff + 1e-9) {
+      best = p;
+      best_eff = eff;
+    }
+  }
+  return best;
+}
+
+bool f32_whole_fits(const GemvPlan& p, int M, int64_t K) {
+  const int64_t blocks = (int64_t)M * (K >> 4);
+  return p.kind == nvfp4::kGemvMfma && blocks <= nvfp4::qa_max_blocks(M, p.waves, true) &&
+         blocks <= kFuseMaxBlocks;
+}
+
+// Whether nvfp4_quantize_linear_f32 with a maxima record takes the K-slice
+// plan ps over the whole-activation plan p (NVFP4_OPT_F32_SLICES).  Off by
+// default: every slice is quantized by each of its workgroups and the
+// split-K tail costs more than it saves (graph replays: Qwen3-32B down at
+// M = 1 17.1 us whole vs 19.9 us in 8 slices; at M = 8 the quantizer with
+// the record then the linear 27.8 us vs 31.8 us in 8 slices; Qwen3-8B down
+// at M = 8 16.6 vs 17.6 us).
+bool f32_take_slices(const GemvPlan& p, const GemvPlan& ps, int M, int64_t K) {
+  if (ps.kind != nvfp4::kGemvMfma) return false;
+  const int64_t mode = g_opts[NVFP4_OPT_F32_SLICES].load();
+  return mode == 2 || (mode == 1 && !f32_whole_fits(p, M, K));
+}
+
+nvfp4_status check_ws(const GemvPlan& p, void* workspace, size_t workspace_bytes) {
+  if (p.ws_bytes == 0) return NVFP4_OK;
+  if (!workspace || !aligned(workspace, 256)) return NVFP4_ERR_INVALID_ARG;
+  return workspace_bytes < p.ws_bytes ? NVFP4_ERR_WORKSPACE : NVFP4_OK;
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_quantize_act_f32(const float* x_f32, int M, int64_t K, int64_t ldx,
+                                    const uint32_t* x_amax, uint8_t* x_codes, uint8_t* x_scales,
+                                    float* x_gscale, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (!x_f32 || !x_codes || !x_scales || !x_gscale) return NVFP4_ERR_INVALID_ARG;
+  if (M < 1 || K < 16 || K % 16 != 0 || (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks ||
+      ldx < K || ldx % 4 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_f32, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
+      (x_amax && !aligned(x_amax, 16)))
+    return NVFP4_ERR_INVALID_ARG;
+  const nvfp4::ActPlan ap = nvfp4::act_plan(M, K);
+  if (ap.groups > 1 && !x_amax) {
+    if (!workspace || !aligned(workspace, 16)) return NVFP4_ERR_INVALID_ARG;
+    if (workspace_bytes < nvfp4::kActSyncBytes) return NVFP4_ERR_WORKSPACE;
+  }
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_quantize_act_f32(
+      x_f32, M, (int)K, ldx, x_amax, x_codes, x_scales, x_gscale,
+      static_cast<uint32_t*>(workspace), (uint32_t)g_opts[NVFP4_OPT_SPIN_LIMIT].load(),
+      (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+size_t nvfp4_quantize_linear_f32_workspace_bytes(int M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxM || !valid_nk(N, K) ||
+      N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN)
+    return 0;
+  const GemvPlan p = make_plan(M, N, K);
+  size_t b = std::max(nvfp4::kActSyncBytes, p.ws_bytes);
+  const GemvPlan ps = f32_slice_plan(M, N, K);
+  if (f32_take_slices(p, ps, M, K)) b = std::max(b, ps.ws_bytes);   // it may run
+  return b;
+}
+
+nvfp4_status nvfp4_quantize_linear_f32(int M, int64_t N, int64_t K, const float* x_f32,
+                                       int64_t ldx, const uint32_t* x_amax,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const float* w_gscale, void* y, int out_dtype,
+                                       uint8_t* x_codes, uint8_t* x_scales, float* x_gscale,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  if (M < 1 || !valid_nk(N, K) || N > (int64_t)nvfp4::kMaxCounterTiles * nvfp4::kTileN ||
+      (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks || ldx < K || ldx % 4 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!x_f32 || !w_codes || !w_scales || !w_gscale || !y || !x_codes || !x_scales || !x_gscale)
+    return NVFP4_ERR_INVALID_ARG;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_f32, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
+      (x_amax && !aligned(x_amax, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 8) ||
+      !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
+    return NVFP4_ERR_INVALID_ARG;
+  const bool fuse = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0;
+  GemvPlan p = make_plan(M, N, K);
+  int qslice = 0;
+  // with the producer's maxima record every workgroup may stay in one K
+  // slice and quantize only that slice (the record's maximum covers them all)
+  const GemvPlan ps = fuse && x_amax ? f32_slice_plan(M, N, K) : GemvPlan{};
+  if (fuse && x_amax && f32_take_slices(p, ps, M, K)) {
+    p = ps;
+    qslice = 1;
+  } else if (!(fuse && f32_whole_fits(p, M, K))) {
+    // two launches: the binary32 activation quantizer, then the linear
+    const nvfp4_status st = nvfp4_quantize_act_f32(x_f32, M, K, ldx, x_amax, x_codes, x_scales,
+                                                   x_gscale, workspace, workspace_bytes, stream);
+    if (st != NVFP4_OK) return st;
+    return nvfp4_linear(M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y,
+                        out_dtype, workspace, workspace_bytes, stream);
+  }
+  if (nvfp4_status st = check_ws(p, workspace, workspace_bytes); st != NVFP4_OK) return st;
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_gemv_stream(
+      p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, y, out_dtype,
+      workspace, (hipStream_t)stream, nullptr, ldx, x_codes, x_scales, x_gscale, 0, 0.0f, nullptr,
+      nullptr, x_f32, x_amax, qslice);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_quantize_linear_silu_mul(int M, int64_t F, int64_t K, const uint16_t* x_bf16,
+                                            int64_t ldx, int rmsnorm, float eps,
+                                            const uint8_t* w_codes, const uint8_t* w_scales,
+                                            const float* w_gscale, float* h, int64_t ldh,
+                                            uint32_t* h_amax, uint16_t* gu_out, uint8_t* x_codes,
+                                            uint8_t* x_scales, float* x_gscale, float* xh_out,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (M > kMaxM) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t N = 2 * F;
+  if (M < 1 || F < 16 || F % 16 != 0 || !valid_nk(N, K) ||
+      (int64_t)M * (K >> 4) > nvfp4::kActMaxBlocks || ldx < K || ldx % 8 != 0 || ldh < F ||
+      ldh % 4 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rmsnorm != 0 && rmsnorm != 1) return NVFP4_ERR_INVALID_ARG;
+  if (rmsnorm && (K > nvfp4::kPrepMaxK || !(eps >= 0.0f) || !std::isfinite(eps)))
+    return NVFP4_ERR_INVALID_ARG;
+  if (!rmsnorm && xh_out) return NVFP4_ERR_INVALID_ARG;
+  if (!x_bf16 || !w_codes || !w_scales || !w_gscale || !h || !h_amax || !x_codes || !x_scales ||
+      !x_gscale)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(x_codes, 8) || !aligned(x_gscale, 4) ||
+      !aligned(w_codes, 16) || !aligned(w_scales, 8) || !aligned(h, 16) ||
+      !aligned(h_amax, 16) || (gu_out && !aligned(gu_out, 2)) || (xh_out && !aligned(xh_out, 16)))
+    return NVFP4_ERR_INVALID_ARG;
+  const GemvPlan p = make_plan(M, N, K, true);
+  if (p.kind != nvfp4::kGemvMfma) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t blocks = (int64_t)M * (K >> 4);
+  const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 &&
+                     blocks <= nvfp4::qa_max_blocks(M, p.waves) && blocks <= kFuseMaxBlocks;
+  if (!fused) {
+    // the (RMS norm +) activation quantizer first; the GEMV then stages its codes
+    const nvfp4_status st =
+        rmsnorm ? nvfp4_rmsnorm_quantize_act(x_bf16, M, K, ldx, eps, x_codes, x_scales, x_gscale,
+                                             xh_out, workspace, workspace_bytes, stream)
+                : nvfp4_quantize_act(x_bf16, M, K, ldx, x_codes, x_scales, x_gscale, workspace,
+                                     workspace_bytes, stream);
+    if (st != NVFP4_OK) return st;
+  }
+  if (nvfp4_status st = check_device(); st != NVFP4_OK) return st;
+  const hipError_t e = nvfp4::launch_gemv_stream(
+      p, M, N, K, x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, h, 0, workspace,
+      (hipStream_t)stream, fused ? x_bf16 : nullptr, ldx, x_codes, x_scales, x_gscale,
+      fused ? rmsnorm : 0, eps, fused ? xh_out : nullptr, nullptr, nullptr, nullptr, 0, h_amax,
+      ldh, gu_out);
+  return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
 namespace {

@@ -51,6 +51,18 @@ struct GemvArgs {
   float* ho;     // optional binary32 h [M][K] (workgroup 0)
   const float* sgs;  // a caller-supplied (static) activation tensor scale: the
                      // prologue then takes no tensor maximum and writes no og
+  // binary32 activation [M][ldx] quantized in the prologue (instead of xb)
+  const float* xf;
+  // the tensor maximum of xf as a record of per-workgroup maxima
+  // [kAmaxSlots] (|x| bit patterns; their maximum is the tensor's), or null
+  const uint32_t* amax_in;
+  int qslice;    // split K with amax_in: each workgroup quantizes only its K slice
+  // SiLU * mul epilogue (gate_up projection, rows [0, F) gate, [F, 2F) up):
+  // y is h [M][ldh] binary32, gu (optional) the bf16 gate_up output [M][N],
+  // amax_out the record of this launch's per-workgroup maxima of |h|
+  uint32_t* amax_out;
+  int64_t ldh;
+  uint16_t* gu;
 };
 
 __device__ inline u32x4 load_codes(const uint8_t* p, bool nt) {

@@ -9,9 +9,17 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K, co
                               const uint8_t* ws, const float* wg, void* y, int out_bf16,
                               void* workspace, hipStream_t s, const uint16_t* xb, int64_t ldx,
                               uint8_t* oc, uint8_t* os, float* og, int rms, float eps,
-                              float* ho, const float* sgs) {
+                              float* ho, const float* sgs, const float* xf,
+                              const uint32_t* amax_in, int qslice, uint32_t* amax_out,
+                              int64_t ldh, uint16_t* gu) {
   GemvArgs a = {};
   a.sgs = sgs;
+  a.xf = xf;
+  a.amax_in = amax_in;
+  a.qslice = qslice;
+  a.amax_out = amax_out;
+  a.ldh = ldh;
+  a.gu = gu;
   a.rms = rms;
   a.eps = eps;
   a.ho = ho;

@@ -27,6 +27,7 @@
 //    slice of a tile to arrive sums the slices in slice order.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gemv_common.hpp"
@@ -152,10 +153,17 @@ __device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g
 // compiler's memory wait counts stay exact: where paths with different
 // numbers of outstanding loads merge, it waits for all of them.
 // QA: 0 = the activation arrives quantized; 1 = the prologue quantizes the
-// bf16 activation; 2 = it applies the unweighted per-row RMS norm first.
-template <int M, int RG, int XS, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall>
+// bf16 activation; 2 = it applies the unweighted per-row RMS norm first;
+// 3 = it quantizes a binary32 activation (with a.qslice, split K: only this
+// workgroup's K slice, the tensor maximum taken from a.amax_in).
+// SILU: the gate_up projection (its weight's rows interleaved in groups of
+// 16) with SiLU * mul applied in the flush.
+template <int M, int RG, int XS, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall,
+          bool SILU = false>
 __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   static_assert(!H16 || (MF && !SPLIT), "half tiles: MFMA kernel, one K slice");
+  static_assert(!SILU || (MF && !SPLIT && !H16), "SiLU * mul: MFMA kernel, whole tiles, one slice");
+  static_assert(QA != 3 || MF, "binary32 activation: MFMA kernel");
   constexpr int GC = H16 ? 8 : 4;             // chunks per ring group
   constexpr int HS = H16 ? 2 : 1;             // items per row tile (16-row halves)
   constexpr int ROWS = kTileN / HS;           // output rows per item
@@ -168,14 +176,18 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const bool nt = a.nontemporal != 0;
   const int kc = a.kc;
   const int row_dw = kc * 32;
+  // MFMA: dwords per activation row of codes, padded by 8 so that the 8
+  // rows' A-operand reads of one chunk fall in different LDS banks
+  const int xs_row = kc * 8 + 8;
   // VALU: x~ as f16 pairs [M][kc * 32 dwords].  MFMA: raw activation codes
-  // [M][kc * 4 blocks][2 dwords], then the E4M3 activation scales as f16
+  // [M][kc * 4 blocks][2 dwords] (rows xs_row dwords apart), then the E4M3
+  // activation scales as f16
   // (every E4M3 value is an f16 value) [kc * 4 blocks][M], padded to a
   // dword.  Either is followed by the reduction slots [batch][NW][M][ROWS]
   // floats.
   uint32_t* xlds = lds;
-  _Float16* sa = reinterpret_cast<_Float16*>(lds + M * kc * 8);
-  float* red = reinterpret_cast<float*>(MF ? lds + M * kc * 8 + (kc * 4 * M + 1) / 2
+  _Float16* sa = reinterpret_cast<_Float16*>(lds + M * xs_row);
+  float* red = reinterpret_cast<float*>(MF ? lds + M * xs_row + (kc * 4 * M + 1) / 2
                                            : lds + M * row_dw);
   const int kb_row = a.K >> 4;
   const int nblk = M * kc * 4;                // activation 16-blocks, padded K
@@ -274,14 +286,22 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const float xg_v = QA ? 0.0f : a.xg[0];
   const float sgs_v = QA && a.sgs ? a.sgs[0] : 0.0f;
   float g = 0.0f;                             // the binary32 product of both tensor scales
-  uint32_t qv[QA ? XPT : 1][8];            // QA: this thread's bf16 activation blocks
+  // QA: this thread's activation blocks (bf16 pairs, or binary32 with QA 3)
+  uint32_t qv[QA ? XPT : 1][QA == 3 ? 16 : 8];
   u32x2 xc0[QA ? 1 : XPT];                    // else: its first quantized activation blocks
   uint32_t xs0[QA ? 1 : XPT];
-  static_assert(QA >= 0 && QA <= 2, "activation prologue mode");
+  uint32_t rec = 0;                           // QA 3: this thread's share of a.amax_in
+  static_assert(QA >= 0 && QA <= 3, "activation prologue mode");
+  // the blocks the prologue quantizes: [kb0, kb0 + kbn) of every row (the
+  // whole row, or with a.qslice this workgroup's K slice: all its items have
+  // slice blockIdx.x % S, the grid being a multiple of S)
+  const bool qslice = SPLIT && QA == 3 && a.qslice != 0;
+  const int kb0 = qslice ? 4 * ((int)blockIdx.x % S) * a.cps : 0;
+  const int kbn = qslice ? min(4 * a.cps, kb_row - kb0) : kb_row;
   auto put = [&](int m, int kb, u32x2 c, uint32_t sc) __attribute__((always_inline)) {
     if constexpr (MF) {
-      xlds[(m * kc * 4 + kb) * 2] = c.x;
-      xlds[(m * kc * 4 + kb) * 2 + 1] = c.y;
+      xlds[m * xs_row + kb * 2] = c.x;
+      xlds[m * xs_row + kb * 2 + 1] = c.y;
       sa[kb * M + m] = (_Float16)e4m3_to_f32(sc);
     } else {
       decode_act_block(c, sc, xlds + m * row_dw + kb * 8);
@@ -296,6 +316,10 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // to the standalone activation quantizer's.
   // (the bf16 loads are issued before the first weight loads, so waiting for
   // them does not wait for the weights)
+  // QA == 3: the activation is binary32 (the SiLU * mul output of the
+  // gate_up GEMV).  With its producer's record of per-workgroup maxima the
+  // tensor maximum comes from the record (the same value), and with slices
+  // a workgroup quantizes only the blocks of its own K slice.
   // QA == 2: h = x * (1 / sqrt(mean_k x^2 + eps)) per row in binary32 (the
   // row sums in a fixed order: per thread its blocks in order, then the wave
   // tree, then the waves in order, the same in every workgroup), then the
@@ -303,7 +327,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // workgroup 0 can write it out.
   auto quantize_prologue = [&]() __attribute__((always_inline)) {
     const int T = 64 * NW;
-    const int nreal = M * kb_row;
+    const int nreal = M * kbn;
     auto& v = qv;
     uint32_t* wred = reinterpret_cast<uint32_t*>(red);
     // the rows' 1 / rms in LDS (a register array indexed by row would be
@@ -325,7 +349,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       for (int r = 0; r < XPT; ++r) {
         if (r > 0 && nreal <= r * T) break;           // uniform: no block r here
         const int i = (int)threadIdx.x + r * T;
-        const int mr = i < nreal ? row_of<M>(i, kb_row) : M;   // M: no row
+        const int mr = i < nreal ? row_of<M>(i, kbn) : M;   // M: no row
         float bs = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -362,10 +386,14 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       uint32_t b;
       if constexpr (QA == 2) {
         float hb[16];
-        block_h(r, row_rinv(i < nreal ? row_of<M>(i, kb_row) : 0), hb);
+        block_h(r, row_rinv(i < nreal ? row_of<M>(i, kbn) : 0), hb);
         b = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) b = max(b, __float_as_uint(hb[e]) & 0x7FFFFFFFu);
+      } else if constexpr (QA == 3) {
+        b = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) b = max(b, v[r][e] & 0x7FFFFFFFu);
       } else {
         b = absmax_bits(v[r]);
       }
@@ -376,20 +404,22 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     if (a.sgs) {                                      // uniform: a static tensor scale
       sg = sgs_v;
     } else {
+      if (QA == 3 && a.amax_in) amax = rec;           // uniform: the producer's maxima
       amax = wave_max_u32(amax);
       if (lane == 0) wred[wave] = amax;
       __syncthreads();
       amax = 0;
       for (int w = 0; w < NW; ++w) amax = max(amax, wred[w]);
-      sg = tensor_scale(QA == 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
+      sg = tensor_scale(QA >= 2 ? __uint_as_float(amax) : bf16_to_f32(amax));
     }
     g = __fmul_rn(sg, wg_v);
-    const bool out = blockIdx.x == 0;
+    // the canonical codes: workgroup 0, or with slices workgroup s < S (slice s)
+    const bool out = qslice ? (int)blockIdx.x < S : blockIdx.x == 0;
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
       const int i = (int)threadIdx.x + r * T;
       if (i < nreal) {
-        const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
+        const int m = row_of<M>(i, kbn), kb = kb0 + i - m * kbn;
         BlockQ q;
         if constexpr (QA == 2) {
           float hb[16];
@@ -401,6 +431,11 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
             for (int e = 0; e < 4; ++e)
               o[e] = make_float4(hb[4 * e], hb[4 * e + 1], hb[4 * e + 2], hb[4 * e + 3]);
           }
+        } else if constexpr (QA == 3) {
+          float hb[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) hb[e] = __uint_as_float(v[r][e]);
+          q = quantize_block_f32(hb, __uint_as_float(bmx[r]), sg);
         } else {
           q = quantize_block_bf16(v[r], bmx[r], sg);
         }
@@ -411,7 +446,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
         }
       }
     }
-    if (out && threadIdx.x == 0 && !a.sgs) *a.og = sg;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && !a.sgs) *a.og = sg;
     const int npad = kc * 4 - kb_row;                 // zero blocks up to the padded K
     for (int i = threadIdx.x; i < M * npad; i += T) {
       const int m = i / npad;
@@ -488,10 +523,44 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // result is the same on every run) and stored: as the output with one K
   // slice, else as the slice's partial sum (device-coherent, combined after
   // the stream), then a barrier before the slots are reused.
+  // SILU: the weight's row tiles interleave the gate and up projections in
+  // groups of 16 (tile t: rows 0..15 gate columns 16t.., rows 16..31 up of
+  // the same columns), so each item holds both factors of its 16 columns.
+  // The flush sums both rows the same way, rounds them to bf16 as the
+  // projection's bf16 output would be, and stores h = silu(gate) * up
+  // (binary32) at column 16t + r.
   int ci = blockIdx.x, jb = 0, done = 0, batch_first = blockIdx.x;
+  uint32_t hmax = 0;                          // SILU: this thread's largest |h|
   Item cit = item(ci);
   auto flush = [&](bool last) __attribute__((always_inline)) {
     __syncthreads();
+    if constexpr (SILU) {
+      constexpr int HALF = kTileN / 2;
+      for (int i = threadIdx.x; i < jb * M * HALF; i += 64 * NW) {
+        const int j = i / (M * HALF), mr = i - j * (M * HALF);
+        const int m = mr / HALF, r = mr - m * HALF;
+        const float* sgt = red + j * (NW * M * ROWS) + m * ROWS + r;
+        const float* sup = sgt + HALF;
+        float vg = sgt[0], vu = sup[0];
+        for (int q = 1; q < NW; ++q) {
+          vg += sgt[q * M * ROWS];
+          vu += sup[q * M * ROWS];
+        }
+        const Item it = item(batch_first + j * G);
+        const int n = it.tile * HALF + r;               // the h column (< F)
+        const uint16_t bg = f32_to_bf16_rne(vg * g), bu = f32_to_bf16_rne(vu * g);
+        if (a.gu) {                                     // [M][2F]: gate, then up columns
+          a.gu[(int64_t)m * a.N + n] = bg;
+          a.gu[(int64_t)m * a.N + (a.N >> 1) + n] = bu;
+        }
+        const float hv = silu_mul(bf16_to_f32(bg), bf16_to_f32(bu));
+        reinterpret_cast<float*>(a.y)[(int64_t)m * a.ldh + n] = hv;
+        hmax = max(hmax, __float_as_uint(hv) & 0x7FFFFFFFu);
+      }
+      if (!last) __syncthreads();
+      jb = 0;
+      return;
+    }
     for (int i = threadIdx.x; i < jb * M * ROWS; i += 64 * NW) {
       const int j = i / (M * ROWS), mn = i - j * (M * ROWS);
       const float* sl = red + j * (NW * M * ROWS) + mn;
@@ -544,7 +613,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   const int ja = 2 * ((ra >> 2) & 1) + (ra & 1);
   const bool a_on = (h == ((ra >> 2) & 1)) && (ma < M);
   const bool a_lo = a_on && (ra & 1) == 0, a_hi = a_on && (ra & 1) != 0;
-  const uint32_t* xa_row = xlds + (ma < M ? ma : 0) * kc * 8 + ja * 2;
+  const uint32_t* xa_row = xlds + (ma < M ? ma : 0) * xs_row + ja * 2;
 
   // H16 A operand (16 x 128, two chunks): lane l holds row r = l % 16, K
   // group l / 16 (32 elements = blocks 2 (l / 16), + 1 of the pair).  Row r
@@ -580,7 +649,7 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
       for (int mp = 0; mp < (M + 1) / 2; ++mp) {
         const int ma = 2 * mp + a16_m;
         const bool on = a16_on && ma < M;
-        const uint32_t* xp = xlds + ((ma < M ? ma : 0) * kc * 4 + ca * 4 + a16_b) * 2;
+        const uint32_t* xp = xlds + (ma < M ? ma : 0) * xs_row + (ca * 4 + a16_b) * 2;
         const uint32_t a0 = xp[0], a1 = xp[1];
         const bool lo = on && (r16 & 1) == 0, hi = on && (r16 & 1) != 0;
         const v8i Aop = {(int)(lo ? a0 : 0u), (int)(lo ? a1 : 0u), (int)(hi ? a0 : 0u),
@@ -682,12 +751,34 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
   // are skipped or zeroed at use), all before the first weight load.
   if constexpr (QA) {
     const int T = 64 * NW;
-    const int nreal = M * kb_row;
+    const int nreal = M * kbn;
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
       const int i = min((int)threadIdx.x + r * T, nreal - 1);
-      const int m = row_of<M>(i, kb_row), kb = i - m * kb_row;
-      load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
+      const int m = row_of<M>(i, kbn), kb = kb0 + i - m * kbn;
+      if constexpr (QA == 3) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.xf + (int64_t)m * a.ldx + 16 * kb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const u32x4 t = src[e];
+          qv[r][4 * e] = t.x;
+          qv[r][4 * e + 1] = t.y;
+          qv[r][4 * e + 2] = t.z;
+          qv[r][4 * e + 3] = t.w;
+        }
+      } else {
+        load_block_bf16(a.xb + (int64_t)m * a.ldx + 16 * kb, qv[r]);
+      }
+    }
+    if constexpr (QA == 3) {
+      // the maxima record, 4 slots per lane (every wave reads all 256); the
+      // same number of loads with no record (then from a valid dummy word)
+      const bool hr = a.amax_in != nullptr;
+      const uint32_t* rp = hr ? a.amax_in + lane : reinterpret_cast<const uint32_t*>(a.wg);
+      uint32_t rv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rv[k] = rp[hr ? 64 * k : 0];
+      rec = hr ? max(max(rv[0], rv[1]), max(rv[2], rv[3])) : 0u;
     }
     __asm__ volatile("" ::: "memory");      // issued before the weight loads, not sunk
   } else {
@@ -724,6 +815,21 @@ __device__ __forceinline__ void stream_body(const GemvArgs& a, uint32_t* lds) {
     }
   }
   if constexpr (SPLIT) split_tail<M>(a, nitem, g, red);
+  if constexpr (SILU) {
+    // the record: this workgroup's largest |h| in its slot, zeros past the grid
+    uint32_t* wm = reinterpret_cast<uint32_t*>(red);
+    const uint32_t w = wave_max_u32(hmax);
+    __syncthreads();                          // the last flush has read the slots
+    if (lane == 0) wm[wave] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t t = 0;
+      for (int q = 0; q < NW; ++q) t = max(t, wm[q]);
+      a.amax_out[blockIdx.x] = t;
+    }
+    if (blockIdx.x == 0)
+      for (int i = G + (int)threadIdx.x; i < kAmaxSlots; i += 64 * NW) a.amax_out[i] = 0u;
+  }
 }
 
 // Launch: blockDim.x = 64 * a.waves (at most stream_max_waves(M) or
@@ -735,26 +841,26 @@ __global__ __launch_bounds__(64 * stream_max_waves(M)) void gemv_stream_kernel(G
   stream_body<M, stream_ring_groups(M), 0, false, SPLIT, 0, false>(a, lds);
 }
 
-template <int M, bool SPLIT, int QA, bool H16, int XPT>
+template <int M, bool SPLIT, int QA, bool H16, int XPT, bool SILU>
 __global__ __launch_bounds__(64 * mfma_max_waves(M)) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
-  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA, H16, XPT>(a, lds);
+  stream_body<M, mfma_ring_groups(M), 1, true, SPLIT, QA, H16, XPT, SILU>(a, lds);
 }
 
-template <int M, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall>
+template <int M, bool MF, bool SPLIT, int QA, bool H16, int XPT = kXptSmall, bool SILU = false>
 hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   const size_t need = stream_lds_need(M, p.kc, p.waves, MF, p.batch, H16 ? kTileN / 2 : kTileN);
   const size_t lds = need > kStreamLdsReserve || p.grid > 256 ? need : kStreamLdsReserve;
   const void* fn;
   if constexpr (MF)
-    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA, H16, XPT>);
+    fn = reinterpret_cast<const void*>(&gemv_mfma_kernel<M, SPLIT, QA, H16, XPT, SILU>);
   else
     fn = reinterpret_cast<const void*>(&gemv_stream_kernel<M, SPLIT>);
   static hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   if constexpr (MF)
-    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA, H16, XPT>), dim3((unsigned)p.grid),
+    hipLaunchKernelGGL((gemv_mfma_kernel<M, SPLIT, QA, H16, XPT, SILU>), dim3((unsigned)p.grid),
                        dim3(64 * p.waves), lds, s, a);
   else
     hipLaunchKernelGGL((gemv_stream_kernel<M, SPLIT>), dim3((unsigned)p.grid),
@@ -762,53 +868,67 @@ hipError_t launch_ms(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The MFMA kernels of one (split, half tiles, blocks per thread) shape for
+// prologue mode qa (0: quantized, 1: bf16, 2: bf16 + RMS norm, 3: binary32)
+// and epilogue (silu: SiLU * mul; whole tiles, one slice, qa <= 2 only).
+template <int M, bool SPLIT, bool H16, int XPT>
+hipError_t launch_mf(int qa, bool silu, const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  if (silu) {
+    if constexpr (!SPLIT && !H16) {
+      switch (qa) {
+        case 0: return launch_ms<M, true, false, 0, false, XPT, true>(p, a, s);
+        case 1: return launch_ms<M, true, false, 1, false, XPT, true>(p, a, s);
+        case 2: return launch_ms<M, true, false, 2, false, XPT, true>(p, a, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (qa) {
+    case 0: return launch_ms<M, true, SPLIT, 0, H16, XPT>(p, a, s);
+    case 1: return launch_ms<M, true, SPLIT, 1, H16, XPT>(p, a, s);
+    case 2: return launch_ms<M, true, SPLIT, 2, H16, XPT>(p, a, s);
+    default:   // binary32 blocks take twice the registers: 4 per thread at most
+      if constexpr (XPT == kXptSmall) return launch_ms<M, true, SPLIT, 3, H16, XPT>(p, a, s);
+      return hipErrorInvalidValue;
+  }
+}
+
 template <int M, bool MF>
 hipError_t launch_m(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if (p.waves < 1 || p.waves > (MF ? mfma_max_waves(M) : stream_max_waves(M)))
     return hipErrorInvalidValue;
   if constexpr (MF) {
-    const int qa = a.xb ? (a.rms ? 2 : 1) : 0;
-    // blocks the prologue loads per thread: real blocks when it quantizes,
-    // blocks of the padded K when it stages a quantized activation
-    const int nb = qa ? M * (a.K >> 4) : M * p.kc * 4;
-    const bool large = M >= 4 && nb > kXptSmall * 64 * p.waves;
-    if (qa && nb > (M >= 4 ? kXptLarge : kXptSmall) * 64 * p.waves) return hipErrorInvalidValue;
+    static_assert(kAmaxSlots == 256, "the record is read as 4 slots per lane");
+    const int qa = a.xf ? 3 : a.xb ? (a.rms ? 2 : 1) : 0;
+    const bool silu = a.amax_out != nullptr;
+    const bool qslice = a.qslice != 0;
+    if (p.h16 && (p.splits != 1 || p.cpw % 8)) return hipErrorInvalidValue;
+    if (silu && (p.splits != 1 || p.h16 || qa == 3 || a.N % kTileN)) return hipErrorInvalidValue;
+    if (qslice && (qa != 3 || p.splits < 2 || p.grid % p.splits || (!a.amax_in && !a.sgs)))
+      return hipErrorInvalidValue;
+    // blocks the prologue loads per thread: real blocks when it quantizes
+    // (of one slice with qslice), blocks of the padded K when it stages a
+    // quantized activation
+    const int nb = qslice ? M * std::min(4 * p.cps, a.K >> 4)
+                   : qa   ? M * (a.K >> 4)
+                          : M * p.kc * 4;
+    const int cap_s = kXptSmall * 64 * p.waves, cap_l = kXptLarge * 64 * p.waves;
+    if (qa && nb > qa_max_blocks(M, p.waves, qa == 3)) return hipErrorInvalidValue;
+    // a quantized activation past the large batch is staged whole first
+    const bool large = M >= 4 && qa != 3 && nb > cap_s && !(qa == 0 && nb > cap_l);
     if constexpr (M >= 4) {
       if (large) {
-        if (p.h16) {
-          if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
-          if (!qa && nb > kXptLarge * 64 * p.waves)   // staged whole before the weights
-            return launch_ms<M, true, false, 0, true>(p, a, s);
-          return qa == 2   ? launch_ms<M, true, false, 2, true, kXptLarge>(p, a, s)
-                 : qa == 1 ? launch_ms<M, true, false, 1, true, kXptLarge>(p, a, s)
-                           : launch_ms<M, true, false, 0, true, kXptLarge>(p, a, s);
-        }
-        if (!qa && nb > kXptLarge * 64 * p.waves)
-          return p.splits > 1 ? launch_ms<M, true, true, 0, false>(p, a, s)
-                              : launch_ms<M, true, false, 0, false>(p, a, s);
-        if (p.splits > 1)
-          return qa == 2   ? launch_ms<M, true, true, 2, false, kXptLarge>(p, a, s)
-                 : qa == 1 ? launch_ms<M, true, true, 1, false, kXptLarge>(p, a, s)
-                           : launch_ms<M, true, true, 0, false, kXptLarge>(p, a, s);
-        return qa == 2   ? launch_ms<M, true, false, 2, false, kXptLarge>(p, a, s)
-               : qa == 1 ? launch_ms<M, true, false, 1, false, kXptLarge>(p, a, s)
-                         : launch_ms<M, true, false, 0, false, kXptLarge>(p, a, s);
+        if (p.h16) return launch_mf<M, false, true, kXptLarge>(qa, silu, p, a, s);
+        return p.splits > 1 ? launch_mf<M, true, false, kXptLarge>(qa, silu, p, a, s)
+                            : launch_mf<M, false, false, kXptLarge>(qa, silu, p, a, s);
       }
     }
-    if (p.h16) {
-      if (p.splits != 1 || p.cpw % 8) return hipErrorInvalidValue;
-      return qa == 2   ? launch_ms<M, true, false, 2, true>(p, a, s)
-             : qa == 1 ? launch_ms<M, true, false, 1, true>(p, a, s)
-                       : launch_ms<M, true, false, 0, true>(p, a, s);
-    }
-    if (qa) {
-      if (p.splits > 1)
-        return qa == 2 ? launch_ms<M, true, true, 2, false>(p, a, s)
-                       : launch_ms<M, true, true, 1, false>(p, a, s);
-      return qa == 2 ? launch_ms<M, true, false, 2, false>(p, a, s)
-                     : launch_ms<M, true, false, 1, false>(p, a, s);
-    }
+    if (p.h16) return launch_mf<M, false, true, kXptSmall>(qa, silu, p, a, s);
+    return p.splits > 1 ? launch_mf<M, true, false, kXptSmall>(qa, silu, p, a, s)
+                        : launch_mf<M, false, false, kXptSmall>(qa, silu, p, a, s);
   }
+  if (a.xb || a.xf || a.amax_out) return hipErrorInvalidValue;   // the VALU dot: quantized input
   return p.splits > 1 ? launch_ms<M, MF, true, 0, false>(p, a, s)
                       : launch_ms<M, MF, false, 0, false>(p, a, s);
 }

@@ -21,7 +21,7 @@ enum GemvKind { kGemvStream = 0, kGemvSplit = 1, kGemvMfma = 2 };
 // LDS bytes of a streaming-kernel workgroup: the activation (MFMA: codes and
 // f16 scales; VALU: f16 x~) plus `batch` item slots of per-wave partial sums.
 inline size_t stream_act_lds(int M, int kc, bool mfma) {
-  return mfma ? (size_t)M * kc * 32 + ((size_t)kc * 4 * M + 1) / 2 * 4
+  return mfma ? (size_t)M * (kc * 32 + 32) + ((size_t)kc * 4 * M + 1) / 2 * 4
               : (size_t)M * kc * 128;
 }
 inline size_t stream_lds_need(int M, int kc, int waves, bool mfma, int batch, int rows = 32) {
@@ -66,6 +66,13 @@ hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uin
                                uint8_t* scales, float* gscale, uint32_t* sync, uint32_t spin_limit,
                                hipStream_t s, const float* sg_static = nullptr);
 
+// The activation quantizer on a binary32 activation; amax_in: the record
+// of per-workgroup maxima its producer wrote (kAmaxSlots), or null.
+hipError_t launch_quantize_act_f32(const float* x, int M, int K, int64_t ldx,
+                                   const uint32_t* amax_in, uint8_t* codes, uint8_t* scales,
+                                   float* gscale, uint32_t* sync, uint32_t spin_limit,
+                                   hipStream_t s);
+
 // Fused stack quantizers (mode 0: RMS norm, 1: SiLU * mul), one workgroup
 // per row of up to 2 * 1024 blocks, K <= kPrepMaxK.
 constexpr int64_t kPrepMaxK = 32768;
@@ -73,8 +80,12 @@ hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64
                                 uint8_t* codes, uint8_t* scales, float* gscale, float* h_out,
                                 uint32_t* sync, uint32_t spin_limit, hipStream_t s);
 
+// gate_up_f > 0: the weight is a gate_up projection [2F][K] (F = gate_up_f)
+// and the tiled rows interleave gate and up in groups of 16: tiled row 32t +
+// r is source row 16t + r (r < 16) or F + 16t + r - 16 (r >= 16).
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                                  uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s);
+                                  uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s,
+                                  int64_t gate_up_f = 0);
 
 hipError_t launch_unpack_weight(const uint8_t* codes, const uint8_t* scales, int64_t N,
                                 int64_t K, uint8_t* codes_rm, uint8_t* scales_rm, hipStream_t s);
@@ -96,7 +107,10 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
                               const uint16_t* xb = nullptr, int64_t ldx = 0,
                               uint8_t* oc = nullptr, uint8_t* os = nullptr,
                               float* og = nullptr, int rms = 0, float eps = 0.0f,
-                              float* ho = nullptr, const float* sgs = nullptr);
+                              float* ho = nullptr, const float* sgs = nullptr,
+                              const float* xf = nullptr, const uint32_t* amax_in = nullptr,
+                              int qslice = 0, uint32_t* amax_out = nullptr, int64_t ldh = 0,
+                              uint16_t* gu = nullptr);
 
 // ReSET temperature (reset.hip): per-row arrival counters (at most
 // kResetMaxRows rows) at the start of the workspace, then the partial
@@ -109,8 +123,16 @@ hipError_t launch_reset_temperature(const float* z, int M, int64_t V, int64_t ld
                                     const int32_t* step_end, float* h_out, float* t_out,
                                     float* z_out, int64_t ldo, void* workspace, hipStream_t s);
 
+// Per-workgroup maxima record of a binary32 activation (the SiLU * mul
+// output of the gate_up GEMV): one |h| bit pattern per workgroup slot, zero
+// past the grid; the tensor maximum is the largest entry.
+constexpr int kAmaxSlots = 256;
+
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
-// (4 bf16 blocks per thread, 8 with four or more rows).
-inline int64_t qa_max_blocks(int M, int waves) { return (int64_t)(M >= 4 ? 8 : 4) * 64 * waves; }
+// (4 bf16 blocks per thread, 8 with four or more rows; binary32 blocks
+// take twice the registers: 4 per thread).
+inline int64_t qa_max_blocks(int M, int waves, bool f32 = false) {
+  return (int64_t)(M >= 4 && !f32 ? 8 : 4) * 64 * waves;
+}
 
 }  // namespace nvfp4

@@ -200,4 +200,13 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 
 __device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// silu(g) * u = g / (1 + e^-g) * u in binary32: a correctly rounded add,
+// divide and multiply around the device exponential.  The one definition of
+// the element operation between the gate_up and down projections, used by
+// the standalone SiLU quantizers and by the gate_up GEMV's fused epilogue.
+__device__ inline float silu_mul(float g, float u) {
+  const float sig = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
+  return __fmul_rn(sig, u);
+}
+
 }  // namespace nvfp4

@@ -156,6 +156,87 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   }
 }
 
+// The same quantizer on a binary32 activation (the SiLU * mul output that
+// the gate_up GEMV writes).  amax_in: that producer's record of per-workgroup
+// maxima (kAmaxSlots |x| bit patterns, zero past its grid); then the tensor
+// maximum is the record's largest entry and no workgroup waits for another.
+// Without it the maxima are combined as above (a workgroup that gives up
+// takes the maximum of the whole tensor alone).
+__device__ inline void load_block_f32(const float* p, float (&h)[16]) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const u32x4 t = q[e];
+    h[4 * e] = __uint_as_float(t.x);
+    h[4 * e + 1] = __uint_as_float(t.y);
+    h[4 * e + 2] = __uint_as_float(t.z);
+    h[4 * e + 3] = __uint_as_float(t.w);
+  }
+}
+
+__device__ inline uint32_t absmax_bits_f32(const float (&h)[16]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m = max(m, __float_as_uint(h[e]) & 0x7FFFFFFFu);
+  return m;
+}
+
+template <int BPT>
+__global__ __launch_bounds__(kActThreads) void act_quant_f32_kernel(
+    const float* __restrict__ x, int M, int K, int64_t ldx, const uint32_t* __restrict__ amax_in,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
+    uint32_t* sync, uint32_t spin_limit) {
+  __shared__ uint32_t red[kActThreads / kWave];
+  __shared__ uint32_t shared_amax;
+  const int nbr = K >> 4;
+  const int nb = M * nbr;
+  const int stride = gridDim.x * kActThreads;
+  const int b0 = blockIdx.x * kActThreads + threadIdx.x;
+  float v[BPT][16];
+  uint32_t bm[BPT];
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int b = min(b0 + r * stride, nb - 1);
+    const int m = b / nbr, j = b - m * nbr;
+    load_block_f32(x + (int64_t)m * ldx + 16 * j, v[r]);
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    bm[r] = absmax_bits_f32(v[r]);
+    amax = max(amax, bm[r]);
+  }
+  if (amax_in) {                                // uniform: the producer's maxima
+    amax = threadIdx.x < kAmaxSlots ? amax_in[threadIdx.x] : 0u;
+    amax = block_reduce_max(amax, red);
+  } else {
+    amax = block_reduce_max(amax, red);
+    if (gridDim.x > 1) {
+      amax = combine_amax(amax, sync, spin_limit, &shared_amax);
+      if (amax == kGaveUp) {                    // the whole tensor, this workgroup alone
+        uint32_t a2 = 0;
+        for (int b = threadIdx.x; b < nb; b += kActThreads) {
+          const int m = b / nbr, j = b - m * nbr;
+          float hh[16];
+          load_block_f32(x + (int64_t)m * ldx + 16 * j, hh);
+          a2 = max(a2, absmax_bits_f32(hh));
+        }
+        amax = block_reduce_max(a2, red);
+      }
+    }
+  }
+  const float sg = tensor_scale(__uint_as_float(amax));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = sg;
+#pragma unroll
+  for (int r = 0; r < BPT; ++r) {
+    const int b = b0 + r * stride;
+    if (b < nb) {
+      const int m = b / nbr, j = b - m * nbr;
+      store_block(codes, scales, K, m, j, quantize_block_f32(v[r], __uint_as_float(bm[r]), sg));
+    }
+  }
+}
+
 // ------------------------------------------------- fused stack quantizers
 //
 // The activation quantizer applied to a binary32 h computed in the same
@@ -197,11 +278,7 @@ __device__ inline void silu_mul_block(const uint16_t* row, int K, int j, float (
   load16_bf16_f32(row + 16 * j, h);
   load16_bf16_f32(row + K + 16 * j, u);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float g = h[i];
-    const float sig = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
-    h[i] = __fmul_rn(sig, u[i]);
-  }
+  for (int i = 0; i < 16; ++i) h[i] = silu_mul(h[i], u[i]);
 }
 
 // h of this thread's blocks of row `row` (blocks past the row are zero)
@@ -379,12 +456,15 @@ __global__ __launch_bounds__(256) void wq_amax_kernel(const uint16_t* __restrict
 
 // One thread per (row tile, K chunk, lane): quantizes the two 16-blocks the
 // lane owns in the tiled layout and writes its 16 code bytes and 2 scale
-// bytes.  Padding rows and columns are written as zeros.
+// bytes.  Padding rows and columns are written as zeros.  gate_up_f > 0: the
+// interleaved gate_up order (tiled row 32t + r <- source row 16t + r for r <
+// 16, F + 16t + r - 16 for r >= 16).
 __global__ __launch_bounds__(256) void wq_blocks_kernel(const uint16_t* __restrict__ w, int64_t N,
                                                         int64_t K, int64_t ldw, int kc, int kg,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales,
-                                                        const uint32_t* __restrict__ slot) {
+                                                        const uint32_t* __restrict__ slot,
+                                                        int64_t gate_up_f) {
   const float sg = tensor_scale(__uint_as_float(*slot));
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rec = gid >> 6;
@@ -395,13 +475,15 @@ __global__ __launch_bounds__(256) void wq_blocks_kernel(const uint16_t* __restri
   const int64_t k0 = (int64_t)c * kChunkK + 32 * (l >> 5);
   u32x4 out = {0u, 0u, 0u, 0u};
   uint32_t sc = 0;
+  const int r = l & 31;
+  const int64_t src = gate_up_f > 0 ? (r < 16 ? 16 * t + r : gate_up_f + 16 * t + (r - 16)) : n;
   if (n < N) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t kb = k0 + 16 * b;
       if (kb < K) {
         uint32_t v[8];
-        load_block_bf16(w + n * ldw + kb, v);
+        load_block_bf16(w + src * ldw + kb, v);
         const BlockQ q = quantize_block_bf16(v, sg);
         out[2 * b] = q.lo;
         out[2 * b + 1] = q.hi;
@@ -517,6 +599,26 @@ hipError_t launch_quantize_act(const uint16_t* x, int M, int K, int64_t ldx, uin
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_act_f32(const float* x, int M, int K, int64_t ldx,
+                                   const uint32_t* amax_in, uint8_t* codes, uint8_t* scales,
+                                   float* gscale, uint32_t* sync, uint32_t spin_limit,
+                                   hipStream_t s) {
+  static_assert(kAmaxSlots <= kActThreads, "one record slot per thread");
+  const ActPlan p = act_plan(M, K);
+  const uint32_t spin = spin_limit ? spin_limit : kActDefaultSpin;
+#define NVFP4_ACT_F32(BPT)                                                                     \
+  hipLaunchKernelGGL(act_quant_f32_kernel<BPT>, dim3(p.groups), dim3(kActThreads), 0, s, x, M, \
+                     K, ldx, amax_in, codes, scales, gscale, sync, spin)
+  switch (p.bpt) {
+    case 1: NVFP4_ACT_F32(1); break;
+    case 2: NVFP4_ACT_F32(2); break;
+    case 4: NVFP4_ACT_F32(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef NVFP4_ACT_F32
+  return hipGetLastError();
+}
+
 int prep_bpt(int64_t K) { return (K >> 4) <= kPrepThreads ? 1 : 2; }
 
 hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64_t ldx, float eps,
@@ -546,7 +648,8 @@ hipError_t launch_prep_quantize(int mode, const uint16_t* x, int M, int K, int64
 }
 
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                                  uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s) {
+                                  uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s,
+                                  int64_t gate_up_f) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
   const int64_t n_pad = round_up(N, kTileN), k_pad = round_up(K, kGroupK);
   const int kc = (int)(k_pad / kChunkK), kg = (int)(k_pad / kGroupK);
@@ -560,7 +663,7 @@ hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t threads = (n_pad / kTileN) * kc * kWave;
   hipLaunchKernelGGL(wq_blocks_kernel, dim3((unsigned)(threads / 256)), dim3(256), 0, s, w, N, K,
-                     ldw, kc, kg, codes, scales, slot);
+                     ldw, kc, kg, codes, scales, slot, gate_up_f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(wq_finalize_kernel, dim3(1), dim3(1), 0, s, slot);
   return hipGetLastError();

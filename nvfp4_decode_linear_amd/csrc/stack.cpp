@@ -7,6 +7,10 @@
 //     -> O -> RMS norm + quantize -> gate_up -> SiLU * mul + quantize
 //     -> down -> x of the next layer
 //
+// With interleaved gate_up weights the SiLU * mul runs in the gate_up GEMV's
+// epilogue (binary32 h and its maxima record) and its quantizer in the down
+// GEMV's prologue; otherwise gate_up writes bf16 and the SiLU quantizer runs
+// on its own.
 // Every linear writes bf16.  There is no attention, residual or weighted
 // norm: the stack exercises the linears and the quantizers between them at
 // the model's shapes, the rest of a layer is out of scope.  The graph holds
@@ -24,6 +28,7 @@
 
 namespace nvfp4 {
 nvfp4_status record_hip_error(hipError_t e);   // abi.cpp: keeps nvfp4_last_hip_error
+bool silu_plan_ok(int M, int64_t F, int64_t K);  // abi.cpp: the fused gate_up has a plan
 }
 
 struct nvfp4_stack {
@@ -36,7 +41,10 @@ struct nvfp4_stack {
   uint16_t* h = nullptr;                // [M][hidden] inter-layer activation
   uint16_t* qkv = nullptr;              // [M][qkv_n]
   uint16_t* o = nullptr;                // [M][hidden]
-  uint16_t* gu = nullptr;               // [M][2 ffn]
+  uint16_t* gu = nullptr;               // [M][2 ffn] (unfused SiLU * mul only)
+  float* hf = nullptr;                  // [M][ffn] binary32 SiLU * mul output (fused)
+  uint32_t* hamax = nullptr;            // its maxima record (fused)
+  bool silu_fused = false;
   uint8_t* a_codes = nullptr;           // [M][kmax / 2]
   uint8_t* a_scales = nullptr;          // [M][kmax / 16]
   float* a_gscale = nullptr;            // 1 float (padded to 256 B)
@@ -55,7 +63,8 @@ nvfp4_status hip_err(hipError_t e) { return nvfp4::record_hip_error(e); }
 void free_all(nvfp4_stack* s) {
   if (s->exec) (void)hipGraphExecDestroy(s->exec);
   if (s->graph) (void)hipGraphDestroy(s->graph);
-  void* bufs[] = {s->h, s->qkv, s->o, s->gu, s->a_codes, s->a_scales, s->a_gscale, s->ws};
+  void* bufs[] = {s->h,       s->qkv,      s->o,        s->gu, s->hf,
+                  s->hamax,   s->a_codes,  s->a_scales, s->a_gscale, s->ws};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
 }
@@ -84,6 +93,18 @@ nvfp4_status enqueue_step(nvfp4_stack* s, void* st) {
                                    w[kO].scales, w[kO].gscale, s->o, NVFP4_OUT_BF16, s->a_codes,
                                    s->a_scales, s->a_gscale, s->ws, s->ws_bytes, st)) != NVFP4_OK)
       break;
+    if (s->silu_fused) {
+      // RMS norm + quantize + gate_up + SiLU * mul, then quantize + down
+      if ((r = nvfp4_quantize_linear_silu_mul(
+               M, c.ffn, c.hidden, s->o, c.hidden, 1, c.eps, w[kGateUp].codes, w[kGateUp].scales,
+               w[kGateUp].gscale, s->hf, c.ffn, s->hamax, nullptr, s->a_codes, s->a_scales,
+               s->a_gscale, nullptr, s->ws, s->ws_bytes, st)) != NVFP4_OK)
+        break;
+      r = nvfp4_quantize_linear_f32(M, c.hidden, c.ffn, s->hf, c.ffn, s->hamax, w[kDown].codes,
+                                    w[kDown].scales, w[kDown].gscale, xout, NVFP4_OUT_BF16,
+                                    s->a_codes, s->a_scales, s->a_gscale, s->ws, s->ws_bytes, st);
+      continue;
+    }
     // RMS norm + quantize + gate_up (one kernel when it fits)
     if ((r = nvfp4_rmsnorm_quantize_linear(M, 2 * c.ffn, c.hidden, s->o, c.hidden, c.eps,
                                            w[kGateUp].codes, w[kGateUp].scales,
@@ -104,7 +125,8 @@ bool valid_config(const nvfp4_stack_config& c) {
   auto ok_dim = [](int64_t v) { return v >= 16 && v % 16 == 0 && v <= 32768; };
   return c.M >= 1 && c.M <= 8 && c.layers >= 1 && c.layers <= 4096 && ok_dim(c.hidden) &&
          ok_dim(c.q_cols) && ok_dim(c.ffn) && c.qkv_n >= c.q_cols && c.qkv_n % 8 == 0 &&
-         c.qkv_n <= (int64_t(1) << 20) && c.eps >= 0.0f && c.eps < 1.0f;
+         c.qkv_n <= (int64_t(1) << 20) && c.eps >= 0.0f && c.eps < 1.0f &&
+         (c.gate_up_interleaved == 0 || c.gate_up_interleaved == 1);
 }
 
 }  // namespace
@@ -121,6 +143,8 @@ nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weigh
     return NVFP4_ERR_INVALID_ARG;
   if (cfg->M > 8) return NVFP4_ERR_UNSUPPORTED;
   if (!valid_config(*cfg)) return NVFP4_ERR_INVALID_ARG;
+  if (cfg->gate_up_interleaved && !nvfp4::silu_plan_ok(cfg->M, cfg->ffn, cfg->hidden))
+    return NVFP4_ERR_UNSUPPORTED;
   for (int i = 0; i < cfg->layers * 4; ++i)
     if (!weights[i].codes || !weights[i].scales || !weights[i].gscale) return NVFP4_ERR_INVALID_ARG;
   nvfp4_stack* s = new (std::nothrow) nvfp4_stack;
@@ -140,14 +164,21 @@ nvfp4_status nvfp4_stack_create(const nvfp4_stack_config* cfg, const nvfp4_weigh
   ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, c.hidden, c.q_cols));
   ws = std::max(ws, nvfp4_quantize_linear_workspace_bytes(M, 2 * c.ffn, c.hidden));
   ws = std::max(ws, nvfp4_linear_workspace_bytes(M, c.hidden, c.ffn));
+  ws = std::max(ws, nvfp4_quantize_linear_f32_workspace_bytes(M, c.hidden, c.ffn));
   s->ws_bytes = ws;
+  s->silu_fused = c.gate_up_interleaved != 0;
   auto alloc = [&](auto** p, size_t bytes) {
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(bytes, 256));
   };
   alloc(&s->h, (size_t)M * c.hidden * 2);
   alloc(&s->qkv, (size_t)M * c.qkv_n * 2);
   alloc(&s->o, (size_t)M * c.hidden * 2);
-  alloc(&s->gu, (size_t)M * 2 * c.ffn * 2);
+  if (s->silu_fused) {
+    alloc(&s->hf, (size_t)M * c.ffn * 4);
+    alloc(&s->hamax, NVFP4_AMAX_RECORD_WORDS * 4);
+  } else {
+    alloc(&s->gu, (size_t)M * 2 * c.ffn * 2);
+  }
   alloc(&s->a_codes, (size_t)M * kmax / 2);
   alloc(&s->a_scales, (size_t)M * kmax / 16);
   alloc(&s->a_gscale, 256);

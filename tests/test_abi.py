@@ -196,7 +196,8 @@ def test_stack_argument_errors(lib, no_gpu):
     class Cfg(ctypes.Structure):
         _fields_ = [("M", ctypes.c_int), ("layers", ctypes.c_int), ("hidden", ctypes.c_int64),
                     ("qkv_n", ctypes.c_int64), ("q_cols", ctypes.c_int64),
-                    ("ffn", ctypes.c_int64), ("eps", ctypes.c_float)]
+                    ("ffn", ctypes.c_int64), ("eps", ctypes.c_float),
+                    ("gate_up_interleaved", ctypes.c_int)]
 
     class W(ctypes.Structure):
         _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
@@ -217,7 +218,8 @@ def test_stack_argument_errors(lib, no_gpu):
         assert f(ctypes.byref(bad), ws, FAKE, FAKE, FAKE, ctypes.byref(out)) == 2
     for bad in (Cfg(0, 2, 512, 768, 512, 1024, 1e-6), Cfg(1, 0, 512, 768, 512, 1024, 1e-6),
                 Cfg(1, 2, 520, 768, 512, 1024, 1e-6), Cfg(1, 2, 512, 500, 512, 1024, 1e-6),
-                Cfg(1, 2, 512, 768, 512, 40000, 1e-6), Cfg(1, 2, 512, 768, 512, 1024, -1.0)):
+                Cfg(1, 2, 512, 768, 512, 40000, 1e-6), Cfg(1, 2, 512, 768, 512, 1024, -1.0),
+                Cfg(1, 2, 512, 768, 512, 1024, 1e-6, 2)):
         assert f(ctypes.byref(bad), ws, FAKE, FAKE, FAKE, ctypes.byref(out)) == 1
     nulls = (W * 8)(*[W(0x1000, 0x1000, 0x1000)] * 7 + [W(0x1000, 0, 0x1000)])
     assert f(ctypes.byref(good), nulls, FAKE, FAKE, FAKE, ctypes.byref(out)) == 1
@@ -364,3 +366,66 @@ def test_reset_temperature_argument_errors(lib, no_gpu):
     assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 3
     tail[5] = 1004                                                            # in place, ldo != ldl
     assert f(FAKE, 1, 1000, 1000, ctypes.byref(good), *tail) == 1
+
+
+def test_silu_and_f32_argument_errors(lib, no_gpu):
+    vp, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    MIS = ctypes.c_void_p(0x1004)
+    g = lib.nvfp4_quantize_weight_gate_up
+    g.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    assert g(FAKE, 24, 512, 512, FAKE, FAKE, FAKE, None) == 1            # F % 16
+    assert g(FAKE, 64, 512, 500, FAKE, FAKE, FAKE, None) == 1            # ldw < K
+    assert g(FAKE, 64, 512, 512, FAKE, FAKE, FAKE, None) == 3            # no device
+    s = lib.nvfp4_quantize_linear_silu_mul
+    s.argtypes = [ctypes.c_int, i64, i64, vp, i64, ctypes.c_int, f32, vp, vp, vp, vp, i64, vp,
+                  vp, vp, vp, vp, vp, vp, sz, vp]
+
+    def silu(M=1, F=1024, K=512, ldx=512, rms=1, eps=1e-6, h=FAKE, ldh=1024, amax=FAKE,
+             xh=None):
+        return s(M, F, K, FAKE, ldx, rms, eps, FAKE, FAKE, FAKE, h, ldh, amax, None, FAKE, FAKE,
+                 FAKE, xh, FAKE, 1 << 20, None)
+    assert silu(M=9) == 2
+    assert silu(F=1000) == 1                                              # F % 16
+    assert silu(ldh=1000) == 1                                            # ldh < F
+    assert silu(ldx=500) == 1                                             # ldx < K
+    assert silu(rms=2) == 1
+    assert silu(rms=0, xh=FAKE) == 1                                      # xh_out needs the norm
+    assert silu(eps=-1.0) == 1
+    assert silu(h=None) == 1 and silu(amax=None) == 1 and silu(amax=MIS) == 1
+    assert silu() == 3                                                    # no device
+    a = lib.nvfp4_quantize_act_f32
+    a.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    assert a(FAKE, 9, 512, 512, None, FAKE, FAKE, FAKE, FAKE, 64, None) == 2
+    assert a(FAKE, 1, 512, 510, None, FAKE, FAKE, FAKE, FAKE, 64, None) == 1     # ldx
+    assert a(FAKE, 1, 512, 516, MIS, FAKE, FAKE, FAKE, FAKE, 64, None) == 1      # record alignment
+    # several workgroups combine their maxima in the workspace unless a record is given
+    assert a(FAKE, 8, 25600, 25600, None, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert a(FAKE, 8, 25600, 25600, None, FAKE, FAKE, FAKE, FAKE, 8, None) == 4
+    assert a(FAKE, 8, 25600, 25600, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 3
+    q = lib.nvfp4_quantize_linear_f32
+    q.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                  vp, sz, vp]
+    ok = (FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1 << 24, None)
+    assert q(9, 5120, 25600, FAKE, 25600, FAKE, *ok) == 2
+    assert q(1, 5120, 25600, FAKE, 25599, FAKE, *ok) == 1               # ldx
+    assert q(1, 5120, 25600, FAKE, 25600, MIS, *ok) == 1                 # record alignment
+    assert q(1, 5120, 25600, FAKE, 25600, FAKE, *ok) == 3                # no device
+    qw = lib.nvfp4_quantize_linear_f32_workspace_bytes
+    qw.argtypes = [ctypes.c_int, i64, i64]
+    qw.restype = sz
+    lw = lib.nvfp4_linear_workspace_bytes
+    # Qwen3-8B down at M = 1: the whole activation fits the prologue of a plan
+    # that fills the CUs: the linear's need (none) or the sync record
+    assert qw(1, 4096, 12288) == 16
+    # M = 8: the two launches' need by default; with the K-slice plan allowed,
+    # its split-K counters and partials
+    assert qw(8, 5120, 25600) == max(16, lw(8, 5120, 25600))
+    lib.nvfp4_set_option.argtypes = [ctypes.c_int, i64]
+    assert lib.nvfp4_set_option(10, 1) == 0
+    try:
+        assert qw(8, 5120, 25600) > max(16, lw(8, 5120, 25600))
+        assert qw(1, 4096, 12288) == 16                  # fits: no slices even then
+    finally:
+        assert lib.nvfp4_set_option(10, 0) == 0
+    assert lib.nvfp4_set_option(10, 3) == 1
+    assert qw(9, 5120, 25600) == 0

@@ -12,6 +12,8 @@ import pytest
 
 import oracle
 from gpu_util import note, to_dev_bf16
+from parity_util import check_linear as _check_linear, check_quant as _check_quant
+from parity_util import sample_rows as _sample_rows
 from workloads import activations_bf16, bf16_to_f32, weights_bf16
 
 pytestmark = pytest.mark.gpu
@@ -25,6 +27,9 @@ CONFIGS = [  # M, hidden, qkv_n, q_cols, ffn, layers
     # activation blocks, past the fused prologue, so the RMS norm and the q
     # slice are quantized by their own kernels on the shared workspace
     (8, 5120, 1024, 1024, 512, 2),
+    # gate_up weights in plain row order: gate_up writes bf16 and the SiLU
+    # quantizer runs on its own (every other config fuses it)
+    (2, 256, 384, 256, 528, 2),
 ]
 # The Qwen3-32B decoder shapes (hidden 5120, QKV 10240, q slice 8192, FFN
 # 25600) of the 64-layer decode step that the "ReSET" GitHub README's demo
@@ -50,6 +55,10 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _fused(cfg):
+    return cfg[4] != 528          # the one config kept on the unfused SiLU path
+
+
 def _weights(nv, cfg):
     M, hidden, qkv_n, q_cols, ffn, layers = cfg
     shapes = [(qkv_n, hidden), (hidden, q_cols), (2 * ffn, hidden), (hidden, ffn)]
@@ -57,15 +66,17 @@ def _weights(nv, cfg):
     for l in range(layers):
         w16 = [weights_bf16(6, 10 * l + j, N, K) for j, (N, K) in enumerate(shapes)]
         src.append(w16)
-        q.append(tuple(nv.quantize_weight(to_dev_bf16(w)) for w in w16))
+        q.append(tuple(nv.quantize_weight_gate_up(to_dev_bf16(w)) if j == 2 and _fused(cfg)
+                       else nv.quantize_weight(to_dev_bf16(w)) for j, w in enumerate(w16)))
     return src, q
 
 
 def _eager(nv, cfg, wq, x, trace=False):
     """The step call by call through the binding (the calls the stack makes:
-    RMS norm + quantize + QKV, quantize + O, RMS norm + quantize + gate_up,
-    SiLU * mul + quantize, down); with trace, the inputs and outputs of every
-    op of every layer."""
+    RMS norm + quantize + QKV, quantize + O, then with interleaved gate_up
+    weights RMS norm + quantize + gate_up + SiLU * mul and quantize + down,
+    else RMS norm + quantize + gate_up, SiLU * mul + quantize, down);
+    with trace, the inputs and outputs of every op of every layer."""
     import torch
     M, hidden, qkv_n, q_cols, ffn, layers = cfg
     ops = []
@@ -76,59 +87,21 @@ def _eager(nv, cfg, wq, x, trace=False):
         qkv, a1 = nv.rmsnorm_quantize_linear(cur, qkv_w, 1e-6, out_dtype=torch.bfloat16, h_out=h1)
         o, a2 = nv.quantize_linear(qkv[:, :q_cols], o_w, out_dtype=torch.bfloat16)
         h3 = torch.empty((M, hidden), dtype=torch.float32, device="cuda")
-        gu, a3 = nv.rmsnorm_quantize_linear(o, gu_w, 1e-6, out_dtype=torch.bfloat16, h_out=h3)
-        h4 = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
-        a4 = nv.silu_mul_quantize_act(gu, h_out=h4)
-        dn = nv.linear(a4, dn_w, out_dtype=torch.bfloat16)
+        if gu_w.gate_up:
+            gu = torch.empty((M, 2 * ffn), dtype=torch.bfloat16, device="cuda") if trace else None
+            h4, rec, a3 = nv.quantize_linear_silu_mul(o, gu_w, rmsnorm=True, eps=1e-6, gu_out=gu,
+                                                      xh_out=h3)
+            dn, a4 = nv.quantize_linear_f32(h4, dn_w, amax=rec, out_dtype=torch.bfloat16)
+        else:
+            gu, a3 = nv.rmsnorm_quantize_linear(o, gu_w, 1e-6, out_dtype=torch.bfloat16, h_out=h3)
+            h4 = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
+            a4 = nv.silu_mul_quantize_act(gu, h_out=h4)
+            dn = nv.linear(a4, dn_w, out_dtype=torch.bfloat16)
         if trace:
             ops.append(dict(x=cur, h1=h1, a1=a1, qkv=qkv, a2=a2, o=o, h3=h3, a3=a3, gu=gu, h4=h4,
                             a4=a4, dn=dn))
         cur = dn
     return cur, ops
-
-
-def _oracle_act(a):
-    return oracle.NVFP4Tensor(a.codes.cpu().numpy(), a.scales.cpu().numpy(),
-                              np.asarray(a.gscale.cpu().numpy()[0], np.float32))
-
-
-def _check_quant(a, h32):
-    ref = oracle.quantize(h32)
-    assert np.array_equal(a.codes.cpu().numpy(), ref.codes)
-    assert np.array_equal(a.scales.cpu().numpy(), ref.scales)
-    assert a.gscale.cpu().numpy().view(np.uint32)[0] == np.asarray(ref.gscale,
-                                                                   np.float32).view(np.uint32)
-
-
-def _sample_rows(N, seed, n=256):
-    """Output columns checked at the large shapes: both ends of the row range
-    (the first and the ragged last tiles) and a random sample."""
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(min(N, 48)), np.arange(max(0, N - 48), N),
-                                     rng.choice(N, min(N, n), replace=False)]))
-
-
-def _check_linear(y_bf16, a, w16, cols=None):
-    """The linear's bf16 output against the oracle on the GPU's quantized
-    activation (itself checked against the oracle quantizer before); the
-    oracle quantizes the weight rows (all, or the sampled `cols`) itself,
-    with the tensor scale of the whole weight."""
-    wf = bf16_to_f32(w16)
-    if cols is None:
-        ow = oracle.quantize(wf)
-    else:
-        _, sg = oracle.global_scale(wf)
-        wc, ws = oracle.quantize_blocks(wf[cols], sg)
-        ow = oracle.NVFP4Tensor(wc, ws, np.asarray(sg, np.float32))
-    ox = _oracle_act(a)
-    ref = oracle.linear_ref(ox, ow)
-    bound = oracle.tolerance_bound(ox, ow) + 0.5 * np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
-    got = y_bf16.float().cpu().numpy().astype(np.float64)
-    if cols is not None:
-        got = got[:, cols]
-    assert np.all(np.isfinite(got))
-    err = np.abs(got - ref)
-    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
 
 
 @pytest.mark.parametrize("cfg", CONFIGS + CONFIGS_32B)
@@ -199,5 +172,10 @@ def test_stack_ops_teacher_forced_vs_oracle(nv, cfg):
         h4 = t["h4"].cpu().numpy()
         ref = oracle.silu_mul(gin.astype(np.float64))
         assert np.all(np.abs(h4 - ref) <= 16 * U32 * np.abs(ref) + 1e-30)
+        if _fused(cfg):
+            # the fused epilogue's h is the standalone SiLU quantizer's on the same bf16 gu
+            h4s = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
+            nv.silu_mul_quantize_act(t["gu"], h_out=h4s)
+            assert np.array_equal(h4.view(np.uint32), h4s.cpu().numpy().view(np.uint32))
         _check_quant(t["a4"], h4)
         _check_linear(t["dn"], t["a4"], w16[3], cs(hidden, 3))
