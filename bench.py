@@ -401,6 +401,7 @@ def main():
     out_extra = {}
     if not args.no_extras:
         out_extra.update(bench_32b_and_stack(args, torch, nv, dev, timer, linear_table))
+        out_extra["reset_temperature"] = bench_reset(torch, nv, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -462,6 +463,48 @@ def kernel_compare(nv, torch, dev, linears, wsets, xs):
                     nv.set_option("kernel", 0)
                 order.append(f"M={M} {L.name} kernel={kern}")
     print("\n".join(order), flush=True)
+
+
+def bench_reset(torch, nv, dev, V=151936, reps=50):
+    """ReSET's step-aware temperature on Qwen3-vocabulary logits (float32
+    [M][151936], 4 x N(0,1)): entropy + step statistics + temperature, and
+    with the scaled logits written to a second buffer; us per call from
+    graph replays.  Bytes: the logits read once by the entropy kernel, and
+    read + written once more by the scaling kernel."""
+    res = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1519)
+    p = nv.ResetParams(0.1, 0.5505, 0.6, 1.5)
+    for Mx in (1, 8):
+        z = torch.randn((Mx, V), generator=gen, device=dev) * 4.0
+        zo = torch.empty_like(z)
+        st = torch.zeros((Mx, 2), dtype=torch.float32, device=dev)
+        row = {}
+        for name, out in (("entropy_temperature", None), ("with_scaled_logits", zo)):
+            s = torch.cuda.Stream(device=dev)
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                nv.reset_temperature(z, p, st, None, out=out)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(reps):
+                    nv.reset_temperature(z, p, st, None, out=out)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (5 * reps)
+            nbytes = Mx * V * 4 * (3 if out is not None else 1)
+            row[name] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        res[f"M{Mx}"] = row
+        progress(f"reset temperature M={Mx}: {row}")
+    return {"V": V, "logits": "float32 4 x N(0,1), resident (4.9 MB at M = 8)", **res}
 
 
 def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):

@@ -256,8 +256,11 @@ nvfp4_status nvfp4_quantize_linear(int M, int64_t N, int64_t K, const uint16_t* 
 /* The unweighted per-row RMS norm, the activation quantizer and the linear
  * in one call: y = linear(Q(h)) with h as for nvfp4_rmsnorm_quantize_act
  * (x_codes, x_scales, x_gscale and, if not NULL, h_out [M][K] binary32 are
- * written).  In one kernel when nvfp4_quantize_linear would fuse; its
- * workgroups then sum each row's squares in their own fixed order (the same
+ * written).  In one kernel when nvfp4_quantize_linear would fuse and the
+ * activation fits 4 blocks per thread at any M (M * K / 16 <= 2048 with 8
+ * wavefronts; at 8 per thread the fused norm measured slower than its own
+ * launch); its workgroups then sum each row's squares in their own fixed
+ * order (the same
  * in every workgroup and on every run, but not the standalone quantizer's,
  * so h may differ from nvfp4_rmsnorm_quantize_act's in the last bits; either
  * way the codes are exactly Q of the h that is written).  Otherwise

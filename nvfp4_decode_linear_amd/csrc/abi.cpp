@@ -430,6 +430,19 @@ size_t nvfp4_quantize_linear_workspace_bytes(int M, int64_t N, int64_t K) {
 
 namespace {
 
+// Whether the GEMV's prologue quantizes the bf16 activation (every workgroup
+// the whole of it) instead of a quantizer launch before the GEMV: up to 4
+// blocks per thread, and without the RMS norm and with four or more rows up
+// to 8 (the E2M1 encoding runs on the conversion instruction; a second
+// launch costs about 5 us at M = 8).  The RMS norm's prologue at 8 blocks
+// per thread cost more than its own launch (Qwen3-32B QKV at M = 8 in the
+// layer stack: 21.1 us fused, 5.8 + 13.0 us as two launches).
+bool fuse_prologue(const GemvPlan& p, int M, int64_t K, bool rms) {
+  const int64_t blocks = (int64_t)M * (K >> 4);
+  return g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
+         blocks <= nvfp4::qa_max_blocks(M, p.waves, rms) && blocks <= kFuseMaxBlocks;
+}
+
 // nvfp4_quantize_linear (rms = 0), nvfp4_rmsnorm_quantize_linear (rms = 1)
 // and, with sg_static set, nvfp4_quantize_linear_static (x_gscale unused)
 nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, const float* sg_static, int M,
@@ -454,13 +467,7 @@ nvfp4_status quantize_linear_impl(int rms, float eps, float* h_out, const float*
       !aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2) || (h_out && !aligned(h_out, 16)))
     return NVFP4_ERR_INVALID_ARG;
   const GemvPlan p = make_plan(M, N, K);
-  // Every workgroup quantizes the whole activation in its prologue: worth it
-  // up to 2048 blocks (4 per thread), and with four or more rows up to 4096
-  // (8 per thread), since the E2M1 encoding runs on the conversion
-  // instruction; the alternative is a second launch (about 5 us at M = 8).
-  const int64_t blocks = (int64_t)M * (K >> 4);
-  const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 && p.kind == nvfp4::kGemvMfma &&
-                     blocks <= nvfp4::qa_max_blocks(M, p.waves) && blocks <= kFuseMaxBlocks;
+  const bool fused = fuse_prologue(p, M, K, rms != 0);
   if (!fused) {
     // two launches: the (RMS norm +) activation quantizer, then the linear
     const nvfp4_status st =
@@ -704,9 +711,7 @@ nvfp4_status nvfp4_quantize_linear_silu_mul(int M, int64_t F, int64_t K, const u
     return NVFP4_ERR_INVALID_ARG;
   const GemvPlan p = make_plan(M, N, K, true);
   if (p.kind != nvfp4::kGemvMfma) return NVFP4_ERR_UNSUPPORTED;
-  const int64_t blocks = (int64_t)M * (K >> 4);
-  const bool fused = g_opts[NVFP4_OPT_FUSE_QUANT].load() != 0 &&
-                     blocks <= nvfp4::qa_max_blocks(M, p.waves) && blocks <= kFuseMaxBlocks;
+  const bool fused = fuse_prologue(p, M, K, rmsnorm != 0);
   if (!fused) {
     // the (RMS norm +) activation quantizer first; the GEMV then stages its codes
     const nvfp4_status st =

@@ -129,10 +129,10 @@ hipError_t launch_reset_temperature(const float* z, int M, int64_t V, int64_t ld
 constexpr int kAmaxSlots = 256;
 
 // Largest M * K / 16 the MFMA streaming kernel quantizes in its prologue
-// (4 bf16 blocks per thread, 8 with four or more rows; binary32 blocks
-// take twice the registers: 4 per thread).
-inline int64_t qa_max_blocks(int M, int waves, bool f32 = false) {
-  return (int64_t)(M >= 4 && !f32 ? 8 : 4) * 64 * waves;
+// (4 bf16 blocks per thread, 8 with four or more rows; `four`: 4 per thread
+// at any M, as binary32 blocks, which take twice the registers, need).
+inline int64_t qa_max_blocks(int M, int waves, bool four = false) {
+  return (int64_t)(M >= 4 && !four ? 8 : 4) * 64 * waves;
 }
 
 }  // namespace nvfp4
