@@ -134,9 +134,20 @@ __device__ __forceinline__ void split_tail(const GemvArgs& a, int nitem, float g
     const int n0 = ((int)blockIdx.x + j * G) / S * kTileN;
     const float* pp = a.part + (int64_t)m * a.n_pad + n0 + n;
     const int64_t st = (int64_t)M * a.n_pad;
+    // the slices' partials in slice order, loaded 8 at a time (all in flight
+    // together: a sum over dependent loads would wait for each in turn)
     float v = 0.0f;
-    for (int t = 0; t < S; ++t)
-      v += __hip_atomic_load(pp + t * st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t0 = 0; t0 < S; t0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        pv[k] = t0 + k < S ? __hip_atomic_load(pp + (t0 + k) * st, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < S) v += pv[k];
+    }
     if (n0 + n < a.N) store_y(a, m, n0 + n, v * g);
   }
   for (int j = threadIdx.x; j < nitem; j += nt) {
