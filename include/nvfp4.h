@@ -470,7 +470,7 @@ nvfp4_status nvfp4_quantize_linear_noalloc(int M, int64_t N, int64_t K, const ui
  * Arguments:
  *   logits      [M][ldl] binary32, 16-byte aligned, ldl >= V, ldl % 4 == 0;
  *               every row holds at least one finite logit and no +inf/NaN
- *   M           1..256 rows;  V >= 1 vocabulary entries per row
+ *   M           1..256 rows;  1 <= V <= 2^20 vocabulary entries per row
  *   params      host pointer; every field finite and > 0
  *   step_state  [M][2] device binary32 (running sum, count), zeroed by the
  *               caller when a sequence starts; updated in place

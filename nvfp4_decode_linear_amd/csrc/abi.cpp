@@ -786,7 +786,7 @@ size_t nvfp4_linear_workspace_bytes(int M, int64_t N, int64_t K) {
 }
 
 size_t nvfp4_reset_workspace_bytes(int M, int64_t V) {
-  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > (int64_t(1) << 40)) return 0;
+  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > nvfp4::kResetMaxV) return 0;
   return nvfp4::kResetCounterBytes +
          (size_t)round_up((int64_t)M * nvfp4::reset_groups_per_row(V) * 16, 256);
 }
@@ -798,7 +798,7 @@ nvfp4_status nvfp4_reset_temperature(const float* logits, int M, int64_t V, int6
                                      size_t workspace_bytes, void* stream) {
   if (!logits || !params || !step_state || !entropy || !temperature)
     return NVFP4_ERR_INVALID_ARG;
-  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > (int64_t(1) << 40) || ldl < V ||
+  if (M < 1 || M > nvfp4::kResetMaxRows || V < 1 || V > nvfp4::kResetMaxV || ldl < V ||
       ldl % 4 != 0)
     return NVFP4_ERR_INVALID_ARG;
   const nvfp4_reset_params& q = *params;

@@ -116,6 +116,7 @@ hipError_t launch_gemv_stream(const GemvPlan& p, int M, int64_t N, int64_t K,
 // kResetMaxRows rows) at the start of the workspace, then the partial
 // (max, sum, weighted sum) of every workgroup: [rows][groups][4] floats.
 constexpr int kResetMaxRows = 256;
+constexpr int64_t kResetMaxV = int64_t(1) << 20;   // 256 groups of 4096 logits per row
 constexpr size_t kResetCounterBytes = (size_t)kResetMaxRows * 4;
 int reset_groups_per_row(int64_t V);
 hipError_t launch_reset_temperature(const float* z, int M, int64_t V, int64_t ldz, float t_low,

@@ -60,8 +60,13 @@ __device__ inline float wave_reduce_sum(float v) {
   return v;
 }
 
+// Rows of up to kEntMaxGroups groups (kResetMaxV = 2^20 logits).
+constexpr int kEntMaxGroups = 256;
+static_assert((int64_t)kEntMaxGroups * kEntPerGroup == kResetMaxV, "vocabulary limit");
+
 __global__ __launch_bounds__(kEntThreads) void entropy_partial_kernel(EntArgs a) {
   __shared__ float red[3][kEntThreads / 64];
+  __shared__ float cpart[3 * kEntMaxGroups];
   __shared__ int last;
   const int c = blockIdx.x, row = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -121,18 +126,25 @@ __global__ __launch_bounds__(kEntThreads) void entropy_partial_kernel(EntArgs a)
     last = old == (uint32_t)(a.C - 1);
   }
   __syncthreads();
-  if (!last || threadIdx.x != 0) return;
-  // the last workgroup of the row: combine the partials in workgroup order
+  if (!last) return;                              // uniform: the workgroup's own flag
+  // the last workgroup of the row: every thread loads partials (all loads in
+  // flight together; one dependent load after another would cost a round
+  // trip each), then thread 0 combines them in workgroup order
   const float* p = a.part + (int64_t)row * a.C * 4;
+  for (int k = threadIdx.x; k < 3 * a.C; k += kEntThreads) {
+    const int g = k / 3, f = k - 3 * g;
+    cpart[k] = __hip_atomic_load(p + 4 * g + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   float M = -INFINITY;
-  for (int k = 0; k < a.C; ++k)
-    M = fmaxf(M, __hip_atomic_load(p + 4 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  for (int k = 0; k < a.C; ++k) M = fmaxf(M, cpart[3 * k]);
   float S = 0.0f, T = 0.0f;
   for (int k = 0; k < a.C; ++k) {
-    const float mk = __hip_atomic_load(p + 4 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mk = cpart[3 * k];
     if (mk == -INFINITY) continue;                 // a workgroup with no logits
-    const float sk = __hip_atomic_load(p + 4 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float tk = __hip_atomic_load(p + 4 * k + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float sk = cpart[3 * k + 1];
+    const float tk = cpart[3 * k + 2];
     const float sh = mk - M;
     const float f = expf(sh);
     S += sk * f;
@@ -199,6 +211,7 @@ hipError_t launch_reset_temperature(const float* z, int M, int64_t V, int64_t ld
   a.tau0 = tau0;
   a.t_base = t_base;
   a.t_max = t_max;
+  if (a.C > kEntMaxGroups) return hipErrorInvalidValue;
   hipLaunchKernelGGL(entropy_partial_kernel, dim3((unsigned)a.C, (unsigned)M), dim3(kEntThreads),
                      0, s, a);
   hipError_t e = hipGetLastError();

@@ -340,6 +340,7 @@ def test_reset_temperature_argument_errors(lib, no_gpu):
     assert w(1, 151936) == 1024 + 768
     assert w(8, 151936) == 1024 + 4864
     assert w(0, 10) == 0 and w(257, 10) == 0 and w(1, 0) == 0
+    assert w(1, 1 << 20) == 1024 + 4096 and w(1, (1 << 20) + 1) == 0    # at most 2^20 per row
     f = lib.nvfp4_reset_temperature
     f.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.POINTER(P), vp, vp, vp, vp, vp, i64, vp,
                   ctypes.c_size_t, vp]
@@ -349,6 +350,8 @@ def test_reset_temperature_argument_errors(lib, no_gpu):
     assert f(FAKE, 0, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
     assert f(FAKE, 257, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
     assert f(FAKE, 1, 1000, 999, ctypes.byref(good), *ok_tail) == 1           # ldl < V
+    v = (1 << 20) + 4
+    assert f(FAKE, 1, v, v, ctypes.byref(good), *ok_tail) == 1                # V > 2^20
     assert f(FAKE, 1, 1000, 1002, ctypes.byref(good), *ok_tail) == 1          # ldl % 4
     assert f(ctypes.c_void_p(0x1008), 1, 1000, 1000, ctypes.byref(good), *ok_tail) == 1
     assert f(FAKE, 1, 1000, 1000, None, *ok_tail) == 1                        # no params

@@ -92,7 +92,7 @@ def test_entropy_qwen3_vocab(nv, M, sigma):
     _check_entropy(h, z)
 
 
-@pytest.mark.parametrize("V", [1, 5, 100, 4095, 4096, 4097, 12289, V_QWEN3 + 3])
+@pytest.mark.parametrize("V", [1, 5, 100, 4095, 4096, 4097, 12289, V_QWEN3 + 3, 1 << 20])
 def test_entropy_ragged_vocab(nv, V):
     note(f"reset entropy ragged V={V}")
     rng = np.random.default_rng(V)
