@@ -8,11 +8,15 @@ weights, in one call (nvfp4_quantize_linear, binary32 out: one kernel whose
 prologue quantizes the activation).
 Weights are quantized once, then copied into enough distinct buffers
 (>= 1.2 GiB) that every step reads weights that are not resident in the
-256 MB Infinity Cache; step i uses copy i mod copies.  Each copy's step is
-captured into a HIP graph and a timed step is one graph replay; a spin
-kernel holds the GPU while the host enqueues the timed replays, so the host's
-launch cost is not part of the measurement.  Inputs are seeded
-synthetic data with the shapes and distributions of that workload.
+256 MB Infinity Cache; step i uses copy i mod copies.  The timed steps run as
+replays of HIP graphs that each hold --graph-steps consecutive steps (36 by
+default: one graph per token over Qwen3-8B's 36 decoder layers, as a decode
+loop replays one graph per token), plus one graph for the remainder, so that
+exactly --steps steps are timed; a spin kernel holds the GPU while the host
+enqueues the timed replays, so the host's launch cost is not part of the
+measurement.  The same steps replayed one graph per step (which adds the
+graph launch's own GPU-side cost to every step) are reported too.  Inputs are
+seeded synthetic data with the shapes and distributions of that workload.
 
 Prints one JSON line with the step's whole-path algorithmic HBM bytes per
 second (value) and:
@@ -92,6 +96,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, help="activation rows of the timed step (1..8)")
+    ap.add_argument("--graph-steps", type=int, default=36,
+                    help="steps per replayed graph in the timed loop (Qwen3-8B: 36 layers)")
     ap.add_argument("--copies-gib", type=float, default=1.2,
                     help="total bytes of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,38 +306,63 @@ def main():
               flush=True)
         return
 
-    # ---- the timed step: per projection act quant + linear, one graph per copy
+    # ---- the timed steps: per projection act quant + linear
     xqs = [nv.empty_act(M, L.K) for L in linears]
     ys = [torch.empty((M, L.N), dtype=torch.float32, device=dev) for L in linears]
     x_m = [x[:M] for x in xs]
 
-    def step_fn(c):
+    def steps_fn(first, count):
+        """Steps first .. first + count - 1 (step i on weight copy i mod copies)."""
         def fn():
-            for li in range(len(linears)):
-                nv.quantize_linear(x_m[li], wsets[c][li], out=ys[li], xq=xqs[li], ws=ws)
+            for k in range(count):
+                c = (first + k) % copies
+                for li in range(len(linears)):
+                    nv.quantize_linear(x_m[li], wsets[c][li], out=ys[li], xq=xqs[li], ws=ws)
         return fn
 
-    step_graphs = [timer.capture(step_fn(c)) for c in range(copies)]
-    with torch.cuda.stream(timer.stream):
-        for i in range(args.warmup):
-            step_graphs[i % copies].replay()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    timer.lead(1.0 + 0.1 * args.steps)       # the host enqueues ahead of the GPU
-    t0 = time.perf_counter()
-    with torch.cuda.stream(timer.stream):
-        t_start.record(timer.stream)
-        for i in range(args.steps):
-            step_graphs[(args.warmup + i) % copies].replay()
-        t_end.record(timer.stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    progress(f"timed step: {args.steps} replays, {ms_step * 1e3:.2f} us per step")
+    def time_steps(graph_for, plan, warm_plan):
+        """Replays `plan` (a list of (first step, count)) after `warm_plan`;
+        returns ms per step and the wall time."""
+        with torch.cuda.stream(timer.stream):
+            for f, n in warm_plan:
+                graph_for(f, n).replay()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        gl = [graph_for(f, n) for f, n in plan]
+        timer.lead(1.0 + 0.1 * len(gl))      # the host enqueues ahead of the GPU
+        t0 = time.perf_counter()
+        with torch.cuda.stream(timer.stream):
+            t_start.record(timer.stream)
+            for g in gl:
+                g.replay()
+            t_end.record(timer.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return t_start.elapsed_time(t_end) / sum(n for _, n in plan), wall
+
+    graphs = {}
+
+    def graph_for(first, count):
+        key = (first % copies, count)
+        if key not in graphs:
+            graphs[key] = timer.capture(steps_fn(*key))
+        return graphs[key]
+
+    S = max(1, args.graph_steps)
+    K = args.steps
+    plan = [(args.warmup + i, min(S, K - i)) for i in range(0, K, S)]
+    warm = [(i, min(S, args.warmup - i)) for i in range(0, args.warmup, S)]
+    ms_step, wall = time_steps(graph_for, plan, warm)
+    progress(f"timed steps: {K} in graphs of {S}, {ms_step * 1e3:.2f} us per step")
+    graphs.clear()
+    # the same steps, one graph replay per step
+    ms_single, _ = time_steps(graph_for, [(args.warmup + i, 1) for i in range(K)],
+                              [(i, 1) for i in range(args.warmup)])
+    progress(f"one graph per step: {ms_single * 1e3:.2f} us per step")
+    graphs.clear()
     step_bytes = sum(step_linear_bytes(M, L.N, L.K) for L in linears)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    del step_graphs
 
     # ---- GEMV-only graphs (the roofline kernel), per projection and M
     def linear_table(lins, sets, Ms, x_src, reps=8):
@@ -426,7 +457,10 @@ def main():
         "config": {"workload": wl, "M": M,
                    "linears": [f"{L.name} {L.N}x{L.K}" for L in linears],
                    "path": "per projection: nvfp4_quantize_linear (activation quantized "
-                           "inside the GEMV, f32 out), one HIP graph replay per step"},
+                           "inside the GEMV, f32 out); HIP graphs of "
+                           f"{args.graph_steps} steps replayed"},
+        "one_graph_per_step": {"ms_per_step": round(ms_single, 5),
+                               "value": round(step_bytes / (ms_single * 1e-3) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": GEMV_KERNEL,
