@@ -595,10 +595,16 @@ def bench_32b_and_stack(args, torch, nv, dev, timer, linear_table):
         lin_act = Mx * (hidden * 2 + q_cols + ffn) * WEIGHT_BYTES_PER_ELEM
         step_b = nl * (wbytes + act + outs + lin_act)
         finite = bool(torch.isfinite(y_out.float()).all().item())
+        # the replayed graph against the same step launched call by call
+        y_graph = y_out.clone()
+        st.run_eager()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y_graph.view(torch.int16), y_out.view(torch.int16)))
         stack[f"M{Mx}"] = {"us_per_step": round(ms * 1e3, 1),
                            "GBps": round(step_b / (ms * 1e-3) / 1e9, 1),
                            "frac": round(step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "replays": args.stack_steps, "output_finite": finite}
+                           "replays": args.stack_steps, "output_finite": finite,
+                           "graph_matches_eager": same}
         st.close()
         del st
         progress(f"stack M={Mx}: {ms * 1e3:.1f} us per step")

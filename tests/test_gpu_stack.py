@@ -5,7 +5,10 @@ between, and, teacher-forced on the first and last layer, every op of the
 step against the oracle (the quantizers bit-exact given their input, the
 linears within the tolerance bound).  Toy widths check every output; the
 Qwen3-32B decoder shapes (two layers at M = 1 and M = 8) check every op of
-both layers, the linears on sampled output columns."""
+both layers, the linears on sampled output columns; and the 64-layer
+Qwen3-32B stack the bench times is checked at full depth (graph against call
+by call, bit for bit; layers 0, 31 and 63 teacher-forced against the
+oracle)."""
 
 import numpy as np
 import pytest
@@ -150,32 +153,77 @@ def test_stack_ops_teacher_forced_vs_oracle(nv, cfg):
     _sync()
     for l in range(layers) if big else sorted({0, layers - 1}):
         note(f"stack teacher-forced layer {l} cfg={cfg}")
-        t = ops[l]
-        w16 = src[l]
-        xin = bf16_to_f32(t["x"].cpu().view(torch.int16).numpy().view(np.uint16))
-        h1 = t["h1"].cpu().numpy()
-        ref = oracle.rms_norm_rows(xin.astype(np.float64))
-        assert np.all(np.abs(h1 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
-        _check_quant(t["a1"], h1)
-        cs = (lambda N, j: _sample_rows(N, 100 * l + j)) if big else (lambda N, j: None)
-        _check_linear(t["qkv"], t["a1"], w16[0], cs(qkv_n, 0))
-        qs = bf16_to_f32(t["qkv"].cpu().view(torch.int16).numpy().view(np.uint16))[:, :q_cols]
-        _check_quant(t["a2"], qs)
-        _check_linear(t["o"], t["a2"], w16[1], cs(hidden, 1))
-        oin = bf16_to_f32(t["o"].cpu().view(torch.int16).numpy().view(np.uint16))
-        h3 = t["h3"].cpu().numpy()
-        ref = oracle.rms_norm_rows(oin.astype(np.float64))
-        assert np.all(np.abs(h3 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
-        _check_quant(t["a3"], h3)
-        _check_linear(t["gu"], t["a3"], w16[2], cs(2 * ffn, 2))
-        gin = bf16_to_f32(t["gu"].cpu().view(torch.int16).numpy().view(np.uint16))
-        h4 = t["h4"].cpu().numpy()
-        ref = oracle.silu_mul(gin.astype(np.float64))
-        assert np.all(np.abs(h4 - ref) <= 16 * U32 * np.abs(ref) + 1e-30)
-        if _fused(cfg):
-            # the fused epilogue's h is the standalone SiLU quantizer's on the same bf16 gu
-            h4s = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
-            nv.silu_mul_quantize_act(t["gu"], h_out=h4s)
-            assert np.array_equal(h4.view(np.uint32), h4s.cpu().numpy().view(np.uint32))
-        _check_quant(t["a4"], h4)
-        _check_linear(t["dn"], t["a4"], w16[3], cs(hidden, 3))
+        _teacher_forced_layer(nv, cfg, ops[l], src[l], l, big)
+
+
+def _teacher_forced_layer(nv, cfg, t, w16, l, big):
+    """Every op of one traced layer against the oracle, each on the GPU's own
+    input to that op: the norms within their ulp bounds, the quantizers
+    bit-exact, the linears within the tolerance (sampled output columns when
+    big)."""
+    import torch
+    M, hidden, qkv_n, q_cols, ffn, layers = cfg
+    xin = bf16_to_f32(t["x"].cpu().view(torch.int16).numpy().view(np.uint16))
+    h1 = t["h1"].cpu().numpy()
+    ref = oracle.rms_norm_rows(xin.astype(np.float64))
+    assert np.all(np.abs(h1 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
+    _check_quant(t["a1"], h1)
+    cs = (lambda N, j: _sample_rows(N, 100 * l + j)) if big else (lambda N, j: None)
+    _check_linear(t["qkv"], t["a1"], w16[0], cs(qkv_n, 0))
+    qs = bf16_to_f32(t["qkv"].cpu().view(torch.int16).numpy().view(np.uint16))[:, :q_cols]
+    _check_quant(t["a2"], qs)
+    _check_linear(t["o"], t["a2"], w16[1], cs(hidden, 1))
+    oin = bf16_to_f32(t["o"].cpu().view(torch.int16).numpy().view(np.uint16))
+    h3 = t["h3"].cpu().numpy()
+    ref = oracle.rms_norm_rows(oin.astype(np.float64))
+    assert np.all(np.abs(h3 - ref) <= 40 * U32 * np.abs(ref) + 1e-38)
+    _check_quant(t["a3"], h3)
+    _check_linear(t["gu"], t["a3"], w16[2], cs(2 * ffn, 2))
+    gin = bf16_to_f32(t["gu"].cpu().view(torch.int16).numpy().view(np.uint16))
+    h4 = t["h4"].cpu().numpy()
+    ref = oracle.silu_mul(gin.astype(np.float64))
+    assert np.all(np.abs(h4 - ref) <= 16 * U32 * np.abs(ref) + 1e-30)
+    if _fused(cfg):
+        # the fused epilogue's h is the standalone SiLU quantizer's on the same bf16 gu
+        h4s = torch.empty((M, ffn), dtype=torch.float32, device="cuda")
+        nv.silu_mul_quantize_act(t["gu"], h_out=h4s)
+        assert np.array_equal(h4.view(np.uint32), h4s.cpu().numpy().view(np.uint32))
+    _check_quant(t["a4"], h4)
+    _check_linear(t["dn"], t["a4"], w16[3], cs(hidden, 3))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_stack_qwen3_32b_full_depth(nv, M):
+    """The 64-layer Qwen3-32B stack the bench times (hidden 5120, QKV 10240,
+    q slice 8192, FFN 25600): one seeded layer's weights copied on the
+    device into 64 distinct layers; the graph-replayed step bit-identical to
+    the same step call by call at full depth, and layers 0, 31 and 63
+    teacher-forced against the oracle (sampled output columns)."""
+    import torch
+    hidden, qkv_n, q_cols, ffn, layers = 5120, 10240, 8192, 25600, 64
+    cfg = (M, hidden, qkv_n, q_cols, ffn, layers)
+    note(f"stack full depth M={M}: weights")
+    shapes = [(qkv_n, hidden), (hidden, q_cols), (2 * ffn, hidden), (hidden, ffn)]
+    w16 = [weights_bf16(9, j, N, K) for j, (N, K) in enumerate(shapes)]
+    q0 = tuple(nv.quantize_weight_gate_up(to_dev_bf16(w)) if j == 2
+               else nv.quantize_weight(to_dev_bf16(w)) for j, w in enumerate(w16))
+    wq = [q0] + [tuple(nv.QuantWeight(w.codes.clone(), w.scales.clone(), w.gscale.clone(), w.N,
+                                      w.K, w.gate_up) for w in q0) for _ in range(layers - 1)]
+    x = to_dev_bf16(activations_bf16(9, M, M, hidden, "normal"))
+    y = torch.empty((M, hidden), dtype=torch.bfloat16, device="cuda")
+    _sync()
+    note(f"stack full depth M={M}: graph and call by call")
+    st = nv.Stack(M, hidden, qkv_n, q_cols, ffn, wq, x, y)
+    try:
+        st.run(2)
+        _sync()
+        ref, ops = _eager(nv, cfg, wq, x, trace=True)
+        _sync()
+        assert np.array_equal(y.cpu().view(torch.int16).numpy(),
+                              ref.cpu().view(torch.int16).numpy())
+        assert np.all(np.isfinite(y.float().cpu().numpy()))
+    finally:
+        st.close()
+    for l in (0, 31, 63):
+        note(f"stack full depth M={M}: teacher-forced layer {l}")
+        _teacher_forced_layer(nv, cfg, ops[l], w16, l, True)
