@@ -120,6 +120,12 @@ def parse():
     return ap.parse_args()
 
 
+def graph_plan(first, steps, per_graph):
+    """Steps first .. first + steps - 1 as graph replays of at most
+    per_graph consecutive steps each: a list of (first step, count)."""
+    return [(first + i, min(per_graph, steps - i)) for i in range(0, steps, per_graph)]
+
+
 def cpu_baseline(linears, cfg, M, kind, budget_s):
     """The oracle as it stands, on a bounded sample: every projection keeps
     its first 1/16 of the weight rows (quantized by the oracle with the
@@ -351,14 +357,14 @@ def main():
 
     S = max(1, args.graph_steps)
     K = args.steps
-    plan = [(args.warmup + i, min(S, K - i)) for i in range(0, K, S)]
-    warm = [(i, min(S, args.warmup - i)) for i in range(0, args.warmup, S)]
+    plan = graph_plan(args.warmup, K, S)
+    warm = graph_plan(0, args.warmup, S)
     ms_step, wall = time_steps(graph_for, plan, warm)
     progress(f"timed steps: {K} in graphs of {S}, {ms_step * 1e3:.2f} us per step")
     graphs.clear()
     # the same steps, one graph replay per step
-    ms_single, _ = time_steps(graph_for, [(args.warmup + i, 1) for i in range(K)],
-                              [(i, 1) for i in range(args.warmup)])
+    ms_single, _ = time_steps(graph_for, graph_plan(args.warmup, K, 1),
+                              graph_plan(0, args.warmup, 1))
     progress(f"one graph per step: {ms_single * 1e3:.2f} us per step")
     graphs.clear()
     step_bytes = sum(step_linear_bytes(M, L.N, L.K) for L in linears)

@@ -1,6 +1,7 @@
 """bench.py's command-line contract on the CPU: it measures one GPU and
-refuses --gpus N > 1 with a message, and its traffic figure is only taken
-from a counter summary recorded on the current GEMV source."""
+refuses --gpus N > 1 with a message, its timed loop covers exactly the
+requested steps in order, and its traffic figure is only taken from a
+counter summary recorded on the current GEMV source."""
 
 import json
 import os
@@ -33,3 +34,14 @@ def test_traffic_summary_matches_source_or_is_ignored():
     else:
         assert traffic is None and "changed" in note
     assert bench.read_traffic(2)[0] is None
+
+
+def test_graph_plan_covers_exactly_the_steps():
+    sys.path.insert(0, ROOT)
+    import bench
+    for first, steps, per in ((20, 200, 36), (0, 20, 36), (5, 7, 1), (0, 72, 36), (3, 1, 8)):
+        plan = bench.graph_plan(first, steps, per)
+        covered = [f + k for f, n in plan for k in range(n)]
+        assert covered == list(range(first, first + steps))
+        assert all(1 <= n <= per for _, n in plan)
+    assert bench.graph_plan(0, 0, 36) == []
