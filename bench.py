@@ -255,8 +255,8 @@ def progress(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the decode linear on a single "
-              "MI355X only (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the decode linear runs on a single MI355X "
+              "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     import torch
 
