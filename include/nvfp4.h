@@ -96,7 +96,9 @@ typedef enum {
   NVFP4_OPT_NONTEMPORAL = 3,  /* 1 (default) = stream weights with
                                  non-temporal loads; 0 = ordinary loads.   */
   NVFP4_OPT_WAVES = 4,        /* 0 = heuristic; else 4, 8 or 16 wavefronts
-                                 per GEMV workgroup (one 32-row tile).     */
+                                 per GEMV workgroup (one 32-row tile); the
+                                 streaming kernels take at most 8 (more is
+                                 clamped to 8), the split kernel 16.       */
   NVFP4_OPT_KERNEL = 5,       /* 0 = heuristic; 1 = persistent streaming
                                  VALU GEMV (whole K per workgroup; M <= 3
                                  and the activation must fit in LDS, else

@@ -144,7 +144,7 @@ GemvPlan make_plan(int M, int64_t N, int64_t K, bool silu = false, int slices = 
       special || force_kernel == 3 || (auto_kind && (M > gemv_max_m || M > 3));
   const bool want_valu = !want_mfma && (force_kernel == 1 || auto_kind) && M <= 3;
   if (want_mfma || want_valu) {
-    const int max_waves = want_mfma ? 8 : (M == 1 ? 16 : 8);  // as compiled
+    const int max_waves = 8;                               // as compiled
     int want = force_waves > 0 ? std::min<int>((int)force_waves, max_waves)
                                : std::min(max_waves, 8);
     // 16-row half tiles (MFMA only, one K slice): twice the work items, for

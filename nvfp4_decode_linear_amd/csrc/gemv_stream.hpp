@@ -8,7 +8,7 @@
 // item 2 (nvfp4r): for M <= 8 rows the FP4 weights are streamed once and
 // every loaded weight serves all M rows.  On gfx950:
 //
-//  * one workgroup of up to 16 wavefronts per CU walks work items blockIdx.x,
+//  * one workgroup of up to 8 wavefronts per CU walks work items blockIdx.x,
 //    blockIdx.x + gridDim.x, ...; an item is a 32-row tile and a K slice
 //    (normally all of K), whose 4-record groups go to the waves round robin;
 //  * every wave keeps 3 groups of 4 weight records (1 KiB each, one 64-lane
@@ -47,12 +47,13 @@ using namespace gemv;
 // quantizes the activation (8 only at four or more rows).
 constexpr int kXptSmall = 4, kXptLarge = 8;
 
-// Waves per workgroup the kernel is compiled for: 16 (<= 128 VGPRs) for one
-// activation row, 8 (<= 256 VGPRs) for two or three rows, whose register
-// footprint does not fit 128 without spilling.  Four or more rows use the
-// split kernel (the streaming one would spill).
+// Waves per workgroup the kernel is compiled for: 8 (<= 256 VGPRs).  Even
+// one activation row does not fit the 128 VGPRs of 16 waves without
+// spilling (26 VGPRs spilled to scratch at M = 1), and the plan runs 8 waves
+// anyway.  Four or more rows use the split kernel (the streaming one would
+// spill).
 constexpr int kStreamMaxM = 3;
-constexpr int stream_max_waves(int M) { return M == 1 ? 16 : 8; }
+constexpr int stream_max_waves(int) { return 8; }
 
 // Groups of 4 weight records (4 KiB) each wave keeps in flight.
 constexpr int stream_ring_groups(int M) { return M == 3 ? 2 : 3; }
